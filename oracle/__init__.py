@@ -1,0 +1,41 @@
+"""fp64 CPU oracle for the one-row affine-quantized decode MLP.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or call anything here.
+The product (the C-ABI library and its Python binding) never does, and this
+package imports nothing from the product: the two share no code.
+
+What it computes (plain definitions, numpy, float64):
+
+* ``quantize_affine`` / ``dequantize`` -- affine group quantization along the
+  input dim, groups of 32/64/128 (meTile docs, "MLX-LM Backend" page, the
+  affine INT8 / 4-bit passages: per-group scales and biases, nibbles).
+* ``pack_*`` / ``unpack_*`` -- the packed byte layouts the GPU path reads.
+* ``gate_up_swiglu`` -- h = silu(W_gate x) * (W_up x) ("Compute-Graph Fusion"
+  page, section "Automatic Gated Epilogues").
+* ``down_residual`` -- y = r + W_down h (same section, residual epilogue;
+  "MLX-LM Backend" page, section "Dispatch Policy", typed residual store).
+* ``add_rmsnorm`` -- s = a + b, n = rms_norm(s, w, eps), both returned
+  ("Compute-Graph Fusion" page, opening GraphBuilder example).
+* ``scaled_error`` -- max|out - ref| / max|ref|, the scale-normalized error
+  ("Compute-Graph Fusion" page, section "Automatic Gated Epilogues").
+
+Pins: every function is checked by ``tests/test_oracle_*.py`` against closed
+forms, textbook values, hand-derived fixtures under ``tests/golden/`` and a
+brute-force rational implementation on tiny inputs.  No function here is
+"parity unpinned".
+"""
+from .quantize import quantize_affine, dequantize, dequantize_dense_bf16
+from .pack import (pack_codes, unpack_codes, pack_scale_bias, unpack_scale_bias,
+                   pack_gate_up, pack_gate_up_scale_bias, pack_dense_gate_up)
+from .mlp import silu, gate_up_swiglu, down_residual, mlp_decode
+from .rmsnorm import round_to_dtype, add_rmsnorm
+from .compare import scaled_error
+
+__all__ = [
+    "quantize_affine", "dequantize", "dequantize_dense_bf16",
+    "pack_codes", "unpack_codes", "pack_scale_bias", "unpack_scale_bias",
+    "pack_gate_up", "pack_gate_up_scale_bias", "pack_dense_gate_up",
+    "silu", "gate_up_swiglu", "down_residual", "mlp_decode",
+    "round_to_dtype", "add_rmsnorm", "scaled_error",
+]

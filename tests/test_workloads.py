@@ -1,0 +1,53 @@
+"""The seeded input generators (CPU): determinism, shapes, storage rounding."""
+import numpy as np
+import torch
+
+import workloads as W
+
+
+def test_weight_bytes_table():
+    assert W.WORKLOADS[1].weight_bytes == 491_520
+    assert W.WORKLOADS[2].weight_bytes == 56_623_104
+    assert W.WORKLOADS[3].weight_bytes == 82_575_360
+    assert W.WORKLOADS[4].weight_bytes == 160_432_128
+    assert W.WORKLOADS[5].weight_bytes == 110_100_480
+
+
+def test_deterministic_and_distinct():
+    w = W.WORKLOADS[1]
+    g1, u1, d1 = W.weights_f32(w, 0)
+    g2, u2, d2 = W.weights_f32(w, 0)
+    assert np.array_equal(g1, g2) and np.array_equal(d1, d2)
+    assert g1.shape == (512, 256) and d1.shape == (256, 512)
+    assert not np.array_equal(g1, u1)
+    g3, _, _ = W.weights_f32(w, 1)
+    assert not np.array_equal(g1, g3)
+    assert abs(float(g1.std()) - 0.05) < 0.002
+
+
+def test_first_row_of_multirow_draw():
+    w = W.WORKLOADS[1]
+    x1, r1 = W.activations(w, 1)
+    x4, r4 = W.activations(w, 4)
+    assert np.array_equal(x1.values[0], x4.values[0])
+
+
+def test_bf16_rounding_matches_torch():
+    a = np.random.default_rng(0).standard_normal(10000).astype(np.float32) * 7
+    act = W.to_storage(a, "bf16")
+    t = torch.from_numpy(a).to(torch.bfloat16)
+    assert np.array_equal(act.raw, t.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(act.values, t.float().numpy())
+
+
+def test_f16_storage():
+    a = np.random.default_rng(1).standard_normal(1000).astype(np.float32)
+    act = W.to_storage(a, "f16")
+    assert act.raw.dtype == np.uint16
+    assert np.array_equal(act.values, a.astype(np.float16).astype(np.float32))
+
+
+def test_rmsnorm_inputs():
+    a, b, nw = W.rmsnorm_inputs(W.WORKLOADS[2])
+    assert a.dtype == "f16" and a.values.shape == (1, 2048)
+    assert nw.values.min() >= 0.5 and nw.values.max() <= 1.5
