@@ -1,0 +1,269 @@
+"""Benchmark of the one-row quantized decode MLP on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the Qwen3-8B-shaped MLP stack -- d = 4096, ffn = 12288, affine
+uint8 weights with groups of 128 along the input dim, 36 independent layer
+weight sets (5.78 GB, far beyond the 256 MB Infinity Cache and the L2s)
+resident in HBM and rotated per call, 1 activation row in bf16.
+One step = one MLP layer decode: the gate/up + SwiGLU kernel and the
+down + residual kernel on layer (step mod 36).  Steps are replayed from a
+HIP graph holding one rotation of 36 layers (the launch-bound inner loop);
+an eager Python-launched pass is timed too and reported beside it.
+
+Prints one JSON line: metric, value (weight-stream GB/s = algorithmic weight
+bytes per layer / time per layer), the time per layer, the fraction of the
+8 TB/s HBM peak, a roofline record for the dominant kernel (gate/up; its
+duration from per-launch HIP events on the launch stream), and the fp64
+CPU oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "µs/MLP layer + weight-stream GB/s (% of 8 TB/s HBM), 1-row decode"
+HBM_PEAK_GBPS = 8000.0
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prepare_sets(wl: W.Workload, n_sets: int):
+    """Draws, quantizes and packs n_sets weight sets on host threads and uploads them."""
+    import torch
+    import quantized_decode_mlp_amd as qdm
+
+    def one(s):
+        g32, u32, d32 = W.weights_f32(wl, s)
+        q, sb = qdm.quantize_pack_gate_up(g32, u32, wl.bits, wl.group)
+        dq, dsb = qdm.quantize_pack_rows(d32, wl.bits, wl.group)
+        return s, q, sb, dq, dsb
+
+    sets = [None] * n_sets
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        for s, q, sb, dq, dsb in ex.map(one, range(n_sets)):
+            gu = qdm.Weight.from_host(wl.ffn, wl.d, wl.bits, wl.group, q, sb)
+            dn = qdm.Weight.from_host(wl.d, wl.ffn, wl.bits, wl.group, dq, dsb)
+            sets[s] = (gu, dn)
+            if (s + 1) % 6 == 0 or s + 1 == n_sets:
+                _log(f"prepared {s + 1}/{n_sets} layer sets ({time.perf_counter() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    return sets
+
+
+def time_steps(run_step, n_layers, steps, warmup, use_graph):
+    """Times exactly `steps` layer steps; returns seconds."""
+    import torch
+    for i in range(warmup):
+        run_step(i % n_layers)
+    torch.cuda.synchronize()
+    if not use_graph:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run_step(i % n_layers)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_layers):
+            run_step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    full, rest = divmod(steps, n_layers)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(full):
+        g.replay()
+    for i in range(rest):
+        run_step(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, g
+
+
+def kernel_event_times(launch, n_layers, launches):
+    """Average device duration of one kernel from per-launch HIP event pairs
+    recorded on the stream the kernel runs on (torch's current stream)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for i in range(min(launches, n_layers)):
+        launch(i % n_layers)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(i % n_layers)
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(ms.mean()) * 1e3, float(np.median(ms)) * 1e3
+
+
+def cpu_baseline(wl: W.Workload, layers: int):
+    """The fp64 oracle (as it stands) on `layers` of the workload's layer sets:
+    dequantize the layer's codes, both projections, SwiGLU, residual.  The
+    oracle's own quantization of those layers is setup, not timed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    x, r = W.activations(wl, 1)
+    total = 0.0
+    for s in range(layers):
+        g32, u32, d32 = W.weights_f32(wl, s)
+        logical = [oracle.quantize_affine(a, wl.bits, wl.group) for a in (g32, u32, d32)]
+        del g32, u32, d32
+        t0 = time.perf_counter()
+        wg, wu, wd = (oracle.dequantize(c, sc, b, wl.group) for c, sc, b in logical)
+        oracle.mlp_decode(x.values, r.values, wg, wu, wd)
+        total += time.perf_counter() - t0
+        del wg, wu, wd, logical
+    us = total / layers * 1e6
+    return {
+        "value": round(wl.weight_bytes / (us * 1e-6) / 1e9, 3),
+        "unit": "GB/s",
+        "us_per_layer": round(us, 1),
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{layers} of the 36 layer sets, one 1-row decode each: fp64 dequantize + "
+                  f"gate/up + SwiGLU + down + residual (numpy; BLAS threads = cores, elementwise "
+                  f"steps single-threaded); host os.cpu_count() = {os.cpu_count()}",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3600)
+    ap.add_argument("--warmup", type=int, default=108)
+    ap.add_argument("--event-launches", type=int, default=360)
+    ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not built)"}))
+        return 2
+
+    import torch
+    import quantized_decode_mlp_amd as qdm
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[4]
+    n_layers = wl.n_sets
+    sets = prepare_sets(wl, n_layers)
+
+    x, r = W.activations(wl, 1)
+    xd = torch.from_numpy(x.raw.view(np.int16)).view(torch.bfloat16).cuda()
+    rd = torch.from_numpy(r.raw.view(np.int16)).view(torch.bfloat16).cuda()
+    ws = torch.empty(qdm.mlp_workspace_bytes(1, wl.ffn), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(rd)
+    h = torch.empty((1, wl.ffn), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        gu, dn = sets[i]
+        qdm.mlp_decode(xd, rd, gu, dn, workspace=ws, out=out)
+
+    # eager (Python-launched) pass
+    t_eager, _ = time_steps(step, n_layers, args.steps, args.warmup, use_graph=False)
+    us_eager = t_eager / args.steps * 1e6
+    _log(f"eager: {us_eager:.2f} us/layer")
+    t, us_graph = t_eager, None
+    if not args.no_graph:
+        t_graph, _ = time_steps(step, n_layers, args.steps, args.warmup, use_graph=True)
+        us_graph = t_graph / args.steps * 1e6
+        _log(f"graph: {us_graph:.2f} us/layer")
+        t = t_graph
+    us = t / args.steps * 1e6
+    gbps = wl.weight_bytes / (us * 1e-6) / 1e9
+
+    # dominant kernel (gate/up: 2/3 of the bytes), per-launch events
+    gu_bytes = 2 * wl.d * wl.ffn * wl.bits // 8 + 8 * (2 * wl.d * wl.ffn // wl.group)
+    dn_bytes = wl.weight_bytes - gu_bytes
+    gu_us, gu_med = kernel_event_times(lambda i: qdm.gemv_gate_up_swiglu(xd, sets[i][0], h_out=h),
+                                       n_layers, args.event_launches)
+    hd = torch.zeros((1, wl.ffn), dtype=torch.float32, device="cuda")
+    dn_us, dn_med = kernel_event_times(lambda i: qdm.gemv_down_residual(hd, rd, sets[i][1], out=out),
+                                       n_layers, args.event_launches)
+    _log(f"gate/up kernel {gu_us:.2f} us, down kernel {dn_us:.2f} us (event means)")
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+
+    # cross-check parity of this very launch configuration on a sampled layer
+    y_dev = qdm.mlp_decode(xd, rd, *sets[17], workspace=ws, out=torch.empty_like(rd))
+    torch.cuda.synchronize()
+    y_sample = y_dev.float().cpu().numpy()
+    finite = bool(np.all(np.isfinite(y_sample)))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("timing the fp64 CPU oracle ...")
+        cpu = cpu_baseline(wl, args.cpu_layers)
+        _log(f"cpu oracle: {cpu['us_per_layer']:.0f} us/layer")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "us_per_layer": round(us, 3),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-8B-shaped MLP decode stack: d=4096, ffn=12288, affine uint8 "
+                        "group 128, 36 independent layer sets rotated per call, 1 row, bf16 "
+                        "activations and output, fp32 accumulation",
+            "d": wl.d, "ffn": wl.ffn, "rows": 1, "bits": wl.bits, "group": wl.group,
+            "layer_sets": n_layers, "weight_bytes_per_layer": wl.weight_bytes,
+            "launch": "hip graph of 36 layers" if us_graph is not None else "eager",
+        },
+        "eager_us_per_layer": round(us_eager, 3),
+        "graph_us_per_layer": None if us_graph is None else round(us_graph, 3),
+        "kernels_us": {"gemv_gate_up_swiglu": round(gu_us, 3), "gemv_down_residual": round(dn_us, 3),
+                       "gate_up_median": round(gu_med, 3), "down_median": round(dn_med, 3)},
+        "roofline": {
+            "kernel": "gemv_gate_up_swiglu",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": gu_bytes,
+        },
+        "cpu_baseline": cpu,
+        "output_finite": finite,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

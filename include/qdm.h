@@ -1,0 +1,197 @@
+/*
+ * qdm.h -- C ABI of the MI355X (gfx950) one-row quantized decode MLP library.
+ *
+ * What the library computes is defined on the meTile documentation pages:
+ *   - "Compute-Graph Fusion", section "Automatic Gated Epilogues": two
+ *     projections share the activation input, the SwiGLU epilogue
+ *     silu(gate) * up is applied on chip, and for one-row decode the
+ *     transformer residual is added inside the down projection.
+ *   - "MLX-LM Backend", section "Dispatch Policy": affine weights keep
+ *     per-group scales and biases (groups of 32, 64, 128 along the input
+ *     dim), 4-bit weights keep their nibbles, dense BF16 weights get an
+ *     interleaved gate/up view; gate and up share each activation load and
+ *     the SwiGLU epilogue precedes the only write of h; the down projection's
+ *     typed store adds the residual; RMSNorm accumulates in FP32.
+ *   - "Compute-Graph Fusion", opening GraphBuilder example: residual add
+ *     followed by RMSNorm keeps the sum as a second output (one
+ *     multi-output kernel).
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (QDM_OK) or a negative qdm_status.  Nothing is printed and no
+ *     exception crosses the ABI.  Every argument is checked before anything
+ *     is launched or written: on error no output byte is touched.
+ *   - Pointers named "device" are device (HBM) addresses owned by the
+ *     caller; "host" pointers are ordinary host memory owned by the caller.
+ *     The library never allocates, frees or synchronizes device memory and
+ *     keeps no global state; calls are thread-safe.
+ *   - GPU work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *     default stream) and the call returns without waiting.  A failed
+ *     launch returns QDM_ERR_HIP.
+ *   - Row-major storage throughout.  bf16 / f16 values are IEEE binary16
+ *     formats stored as 16-bit words.
+ *
+ * Weight formats (the `bits` field of qdm_weight):
+ *   8  : affine uint8 codes, one per byte, row-major [n][k];
+ *   4  : affine 4-bit codes, two per byte, row-major [n][k/2]; byte i of a row
+ *        holds code 2i in its low nibble and code 2i+1 in its high nibble;
+ *   16 : dense bf16 weights [n][k] (no scale/bias; group = 0).
+ * Affine value of code q in group j of row i:  w = scale[i][j]*q + bias[i][j]
+ * with fp32 (scale, bias) stored as adjacent pairs, [n][k/group][2].
+ * Gate/up pairs are interleaved by rows: packed row 2f is gate row f and
+ * packed row 2f+1 is up row f, for the codes ([ffn][2][...]) and for the
+ * scale/bias pairs ([ffn][2][d/group][2]).
+ */
+#ifndef QDM_H
+#define QDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qdm_status {
+    QDM_OK = 0,
+    QDM_ERR_INVALID_ARG = -1,   /* NULL pointer, non-positive or inconsistent size, non-finite weight */
+    QDM_ERR_UNSUPPORTED = -2,   /* valid but not provided: bits/group/dtype/row-count combination */
+    QDM_ERR_ALIGNMENT = -3,     /* a pointer is not aligned as the entry point requires */
+    QDM_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than qdm_mlp_workspace_bytes() */
+    QDM_ERR_HIP = -5            /* the HIP runtime refused a launch */
+} qdm_status;
+
+typedef enum qdm_dtype { QDM_F32 = 0, QDM_F16 = 1, QDM_BF16 = 2 } qdm_dtype;
+
+/* A packed weight matrix in device memory, described once per weight set and
+ * reused for every call (the pages bind prepared weights once into a warmed
+ * executor: "MLX-LM Backend", "Dispatch Policy").
+ *   n, k        logical shape [n][k]; the contraction runs over k.  For a
+ *               gate/up pair descriptor n = ffn (the number of pairs) and
+ *               k = d.
+ *   bits        8, 4 or 16 (see above).
+ *   group       32, 64 or 128 for bits 8/4 (k % group == 0); 0 for bits 16.
+ *   q           device, 16-byte aligned: packed codes or bf16 words.
+ *   scale_bias  device, 8-byte aligned: fp32 pairs; NULL for bits 16.    */
+typedef struct qdm_weight {
+    int32_t n;
+    int32_t k;
+    int32_t bits;
+    int32_t group;
+    const void* q;
+    const float* scale_bias;
+} qdm_weight;
+
+/* ----------------------------------------------------------------- sizes */
+
+/* Bytes of one packed [n][k] code matrix (bits 4/8) or bf16 matrix (bits 16);
+ * 0 if the arguments are invalid. */
+size_t qdm_packed_q_bytes(int32_t n, int32_t k, int32_t bits);
+
+/* Number of fp32 values of the scale/bias pairs of an [n][k] matrix: 2*n*k/group;
+ * 0 if invalid. */
+size_t qdm_scale_bias_floats(int32_t n, int32_t k, int32_t group);
+
+/* Workspace bytes qdm_mlp_decode needs for m rows: the fp32 hidden row(s)
+ * h[m][ffn], rounded up to 256 bytes; 0 if invalid. */
+size_t qdm_mlp_workspace_bytes(int32_t m, int32_t ffn);
+
+/* ----------------------------------------------------------------- host: quantize / pack
+ * Ahead-of-time preparation, once per weight set, on host buffers.  The pages
+ * prepare packed views ahead of time and keep the originals ("MLX-LM Backend",
+ * intro and "Dispatch Policy"); inputs are never modified.  These run on host
+ * threads and are bit-exact: the same inputs always give the same bytes.
+ *
+ * Quantizer (the pages name an affine format with per-group scale and bias but
+ * print no formula; this is the plain reading): for each row and group,
+ *   mn, mx = min, max of the group's fp32 weights (a zero minimum is stored as +0)
+ *   scale  = (float)(((double)mx - (double)mn) / (2^bits - 1))   nearest-even
+ *   bias   = mn
+ *   q      = clamp(nearbyint(((double)w - (double)mn) / (double)scale), 0, 2^bits - 1)
+ *   and q = 0 for the whole group when scale == 0.                          */
+
+/* w host fp32 [n][k] -> codes host uint8 [n][k], scale/bias host fp32 [n][k/group].
+ * INVALID_ARG for NULLs, non-positive sizes, k % group != 0, or a non-finite
+ * weight; UNSUPPORTED for bits not in {4, 8} or group not in {32, 64, 128}. */
+int qdm_quantize_affine(const float* w, int32_t n, int32_t k, int32_t bits, int32_t group,
+                        uint8_t* codes, float* scale, float* bias);
+
+/* Logical codes/scale/bias -> packed codes q_out (host, qdm_packed_q_bytes bytes)
+ * and scale_bias_out (host, qdm_scale_bias_floats floats).  This is the repack
+ * that keeps codes, scales and biases unchanged (no requantization).
+ * INVALID_ARG also for a code >= 2^bits. */
+int qdm_pack_rows(const uint8_t* codes, const float* scale, const float* bias,
+                  int32_t n, int32_t k, int32_t bits, int32_t group,
+                  void* q_out, float* scale_bias_out);
+
+/* Quantize and pack in one pass: w host fp32 [n][k] -> q_out, scale_bias_out. */
+int qdm_quantize_pack_rows(const float* w, int32_t n, int32_t k, int32_t bits, int32_t group,
+                           void* q_out, float* scale_bias_out);
+
+/* Gate and up matrices (each host fp32 [ffn][d]) -> interleaved packed codes
+ * q_out [ffn][2][d*bits/8] and scale_bias_out [ffn][2][d/group][2]. */
+int qdm_quantize_pack_gate_up(const float* w_gate, const float* w_up, int32_t ffn, int32_t d,
+                              int32_t bits, int32_t group, void* q_out, float* scale_bias_out);
+
+/* Same from logical codes/scales/biases (repack without requantizing). */
+int qdm_pack_gate_up(const uint8_t* gate_codes, const float* gate_scale, const float* gate_bias,
+                     const uint8_t* up_codes, const float* up_scale, const float* up_bias,
+                     int32_t ffn, int32_t d, int32_t bits, int32_t group,
+                     void* q_out, float* scale_bias_out);
+
+/* Dense bf16 gate and up [ffn][d] (host uint16 words) -> interleaved
+ * out [ffn][2][d] (the interleaved gate/up view of "Dispatch Policy"). */
+int qdm_pack_dense_gate_up(const uint16_t* gate_bf16, const uint16_t* up_bf16,
+                           int32_t ffn, int32_t d, uint16_t* out);
+
+/* ----------------------------------------------------------------- device: the hot path
+ * Supported combinations (anything else returns QDM_ERR_UNSUPPORTED):
+ *   act     QDM_F32, QDM_BF16 or QDM_F16: the dtype of x, r and out.
+ *   weights bits 8 or 4 with group 32/64/128, or bits 16 (dense bf16).
+ *   m       1..16 rows.
+ *   k       a multiple of 16 (bits 8), 32 (bits 4) or 8 (bits 16).
+ * Device pointers x, r, out, h, s_out, n_out, a, b, w must be 16-byte aligned. */
+
+/* h[m][ffn] = silu(G) * U with G = x W_gate^T, U = x W_up^T, fp32 accumulation,
+ * one write of h (fp32) per element.
+ *   x        device, act dtype, [m][d]
+ *   gate_up  interleaved pair descriptor (n = ffn, k = d)
+ *   h_out    device fp32 [m][ffn]                                            */
+int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act,
+                            const qdm_weight* gate_up, float* h_out, void* stream);
+
+/* out[m][d] = r + h W_down^T, fp32 accumulation, the residual added in fp32 and
+ * the sum rounded once (nearest-even) to the act dtype.
+ *   h     device fp32 [m][ffn];  r, out: device, act dtype, [m][d]
+ *   down  descriptor with n = d, k = ffn.   out may not alias h; it may alias r. */
+int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype act,
+                           const qdm_weight* down, void* out, void* stream);
+
+/* The whole MLP: the two launches above on one stream, h kept in `workspace`
+ * (device, >= qdm_mlp_workspace_bytes(m, ffn) bytes, 16-byte aligned).
+ * gate_up->k must equal down->n (= d) and gate_up->n must equal down->k (= ffn);
+ * both descriptors must use the same bits. */
+int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
+                   const qdm_weight* gate_up, const qdm_weight* down,
+                   void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* Residual add + RMSNorm with both outputs, per row:
+ *   s = a + b rounded once to `dtype`;  n = s * w / sqrt(mean(s^2) + eps)
+ * with fp32 accumulation of the mean square; n rounded once to `dtype`.
+ *   a, b, s_out, n_out: device, dtype, [rows][n];  w: device, dtype, [n]
+ *   eps >= 0 and finite.  s_out may alias a or b. */
+int qdm_add_rmsnorm(const void* a, const void* b, const void* w, int32_t rows, int32_t n,
+                    float eps, qdm_dtype dtype, void* s_out, void* n_out, void* stream);
+
+/* ----------------------------------------------------------------- misc */
+
+/* A static string naming a status code. */
+const char* qdm_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int qdm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDM_H */

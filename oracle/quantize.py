@@ -10,7 +10,7 @@ one consistent with "scale" and "bias" and with w = scale*q + bias):
     per row n and group j (columns [j*g, (j+1)*g)):
         mn, mx  = min, max of the fp32 weights          (exact)
         scale   = fp32( (fp64(mx) - fp64(mn)) / (2^bits - 1) )   nearest-even
-        bias    = mn
+        bias    = mn      (a zero minimum is stored as +0)
         q       = clamp( rint( (fp64(w) - fp64(bias)) / fp64(scale) ), 0, 2^bits-1 )
     if the fp32 scale is 0 (mx == mn, or the range underflows): all q = 0.
 
@@ -46,6 +46,7 @@ def quantize_affine(w, bits: int, group: int):
     span = mx.astype(np.float64) - mn.astype(np.float64)
     scale = (span / np.float64(qmax)).astype(np.float32)
     bias = mn.copy()
+    bias[bias == 0] = np.float32(0.0)       # -0 and +0 minima are stored alike
     live = scale != 0
     denom = np.where(live, scale.astype(np.float64), 1.0)[..., None]
     t = (wg.astype(np.float64) - bias.astype(np.float64)[..., None]) / denom

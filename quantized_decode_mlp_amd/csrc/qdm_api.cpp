@@ -1,0 +1,115 @@
+// C-ABI entry points of the device path: argument validation, then dispatch to
+// the HIP launchers.  Every check runs before anything is launched, so a
+// rejected call writes nothing.  Host C++ only (no HIP headers needed here).
+#include <cmath>
+#include <cstdint>
+
+#include "qdm.h"
+#include "qdm_internal.h"
+
+namespace {
+
+constexpr int kMaxRows = 16;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_dtype(int dt) { return dt == QDM_F32 || dt == QDM_F16 || dt == QDM_BF16; }
+
+// Checks a weight descriptor; n_expect / k_expect < 0 means "any".
+int check_weight(const qdm_weight* w) {
+    if (!w || !w->q || w->n <= 0 || w->k <= 0) return QDM_ERR_INVALID_ARG;
+    if (w->bits == 16) {
+        if (w->group != 0) return QDM_ERR_INVALID_ARG;
+        if (w->k % 8) return QDM_ERR_UNSUPPORTED;
+    } else if (w->bits == 8 || w->bits == 4) {
+        if (!(w->group == 32 || w->group == 64 || w->group == 128)) return QDM_ERR_UNSUPPORTED;
+        if (w->k % w->group) return QDM_ERR_INVALID_ARG;
+        if (!w->scale_bias) return QDM_ERR_INVALID_ARG;
+        if (!aligned(w->scale_bias, 8)) return QDM_ERR_ALIGNMENT;
+    } else {
+        return QDM_ERR_UNSUPPORTED;
+    }
+    if (!aligned(w->q, 16)) return QDM_ERR_ALIGNMENT;
+    return QDM_OK;
+}
+
+int check_rows(int32_t m) { return (m >= 1 && m <= kMaxRows) ? QDM_OK : (m < 1 ? QDM_ERR_INVALID_ARG : QDM_ERR_UNSUPPORTED); }
+
+int hip_status(int e) { return e == 0 ? QDM_OK : QDM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t qdm_mlp_workspace_bytes(int32_t m, int32_t ffn) {
+    if (m <= 0 || ffn <= 0) return 0;
+    const size_t b = static_cast<size_t>(m) * static_cast<size_t>(ffn) * sizeof(float);
+    return (b + 255) & ~static_cast<size_t>(255);
+}
+
+int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act, const qdm_weight* gate_up,
+                            float* h_out, void* stream) {
+    if (!x || !h_out) return QDM_ERR_INVALID_ARG;
+    if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
+    if (int e = check_rows(m)) return e;
+    if (int e = check_weight(gate_up)) return e;
+    if (!aligned(x, 16) || !aligned(h_out, 16)) return QDM_ERR_ALIGNMENT;
+    return hip_status(qdm::launch_gate_up_swiglu(x, m, act, *gate_up, h_out, stream));
+}
+
+int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype act,
+                           const qdm_weight* down, void* out, void* stream) {
+    if (!h || !r || !out) return QDM_ERR_INVALID_ARG;
+    if (static_cast<const void*>(h) == out) return QDM_ERR_INVALID_ARG;
+    if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
+    if (int e = check_rows(m)) return e;
+    if (int e = check_weight(down)) return e;
+    if (!aligned(h, 16) || !aligned(r, 16) || !aligned(out, 16)) return QDM_ERR_ALIGNMENT;
+    return hip_status(qdm::launch_down_residual(h, r, m, act, *down, out, stream));
+}
+
+int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
+                   const qdm_weight* gate_up, const qdm_weight* down,
+                   void* workspace, size_t workspace_bytes, void* out, void* stream) {
+    if (!x || !r || !out) return QDM_ERR_INVALID_ARG;
+    if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
+    if (int e = check_rows(m)) return e;
+    if (int e = check_weight(gate_up)) return e;
+    if (int e = check_weight(down)) return e;
+    if (gate_up->k != down->n || gate_up->n != down->k) return QDM_ERR_INVALID_ARG;
+    if (gate_up->bits != down->bits) return QDM_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < qdm_mlp_workspace_bytes(m, gate_up->n)) return QDM_ERR_WORKSPACE;
+    if (workspace == out) return QDM_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(r, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+        return QDM_ERR_ALIGNMENT;
+    float* h = static_cast<float*>(workspace);
+    if (int e = qdm::launch_gate_up_swiglu(x, m, act, *gate_up, h, stream)) return hip_status(e);
+    return hip_status(qdm::launch_down_residual(h, r, m, act, *down, out, stream));
+}
+
+int qdm_add_rmsnorm(const void* a, const void* b, const void* w, int32_t rows, int32_t n,
+                    float eps, qdm_dtype dtype, void* s_out, void* n_out, void* stream) {
+    if (!a || !b || !w || !s_out || !n_out) return QDM_ERR_INVALID_ARG;
+    if (rows <= 0 || n <= 0 || !valid_dtype(dtype)) return QDM_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.0f) return QDM_ERR_INVALID_ARG;
+    if (s_out == n_out || n_out == a || n_out == b) return QDM_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(w, 16) || !aligned(s_out, 16) || !aligned(n_out, 16))
+        return QDM_ERR_ALIGNMENT;
+    return hip_status(qdm::launch_add_rmsnorm(a, b, w, rows, n, eps, dtype, s_out, n_out, stream));
+}
+
+const char* qdm_status_string(int status) {
+    switch (status) {
+        case QDM_OK: return "ok";
+        case QDM_ERR_INVALID_ARG: return "invalid argument";
+        case QDM_ERR_UNSUPPORTED: return "unsupported combination";
+        case QDM_ERR_ALIGNMENT: return "misaligned pointer";
+        case QDM_ERR_WORKSPACE: return "workspace missing or too small";
+        case QDM_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int qdm_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,248 @@
+// One-row (and few-row) quantized GEMV kernels for gfx950: gate/up with the
+// SwiGLU epilogue, and down with the residual epilogue.
+//
+// Pages: meTile docs, "Compute-Graph Fusion", section "Automatic Gated
+// Epilogues" (two projections sharing the activation, silu(gate) * up on chip,
+// residual added inside the one-row down projection); "MLX-LM Backend",
+// section "Dispatch Policy" (gate and up share each activation load, SwiGLU
+// before the only write of h, typed residual store; tunables: outputs per
+// SIMD-group, SIMD-groups per threadgroup, K unroll).
+//
+// CDNA4 mapping.  A block is S wave64s that own the same R output rows (R
+// gate/up pairs, or R down rows).  A row's packed bytes are cut into 16-byte
+// chunks; one K-tile is 64 consecutive chunks (1 KiB per row), so a wave's
+// dwordx4 load of one row is fully coalesced.  The S waves of a block take
+// the K-tiles round robin, each keeping fp32 partial sums for every
+// (row, activation row) in registers.  For affine weights a 16-byte chunk
+// always lies inside one group (16/32 codes vs groups of >= 32), so its dot
+// product is folded as scale * sum(q*x) + bias * sum(x): one fp32 FMA per
+// weight plus two per chunk.  Partials are reduced across the wave with
+// shuffles, then across the S waves through LDS, in a fixed order (results
+// are bitwise reproducible); one lane per output applies the epilogue.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qdm_device.h"
+#include "qdm_internal.h"
+
+namespace qdm {
+namespace {
+
+constexpr int kWaves = 4;   // S: waves per block, splitting K
+constexpr int kRows = 4;    // R: outputs (pairs for gate/up) per block
+
+// Adds the contribution of one packed dword (EPD codes) for every activation row.
+// xv[m][e] are the EPD activations matching the dword's codes.
+template <int BITS, int M, int EPD>
+__device__ __forceinline__ void dot_dword(uint32_t w, const float (&xv)[M][EPD], float (&dot)[M]) {
+#pragma unroll
+    for (int e = 0; e < EPD; ++e) {
+        float c;
+        if constexpr (BITS == 8) c = static_cast<float>((w >> (8 * e)) & 0xffu);
+        else if constexpr (BITS == 4) c = static_cast<float>((w >> (4 * e)) & 0xfu);
+        else c = (e == 0) ? __uint_as_float(w << 16) : __uint_as_float(w & 0xffff0000u);
+#pragma unroll
+        for (int m = 0; m < M; ++m) dot[m] = fmaf(c, xv[m][e], dot[m]);
+    }
+}
+
+// GU: gate/up pairs (q rows interleaved [n][2][k]), epilogue h = silu(g) * u (fp32 out).
+// !GU: single rows, epilogue out = r + acc rounded to ODT.
+template <int BITS, int XDT, int ODT, int M, bool GU>
+__global__ void __launch_bounds__(64 * kWaves)
+qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
+             const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
+             int n_out, int k, int gshift, int m_rows) {
+    constexpr int E = 128 / BITS;   // codes per 16-byte chunk
+    constexpr int EPD = E / 4;      // codes per dword
+    constexpr int NV = GU ? 2 : 1;
+    constexpr int R = kRows;
+    constexpr bool AFFINE = BITS != 16;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row0 = blockIdx.x * R;
+    const int nrows = min(R, n_out - row0);
+    const int64_t rb = static_cast<int64_t>(k) * BITS / 8;   // bytes per packed row
+    const int C = static_cast<int>(rb >> 4);                  // chunks per row
+    const int T = (C + 63) >> 6;                              // K-tiles
+    const int ng = AFFINE ? (k >> gshift) : 0;
+
+    float acc[NV][R][M];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[v][r][m] = 0.f;
+
+    for (int t = wave; t < T; t += kWaves) {
+        const int c = (t << 6) + lane;
+        if (c < C) {
+            const int k0 = c * E;
+            // issue every weight load of this tile first
+            uint4 wq[R][NV];
+            float2 p[R][NV];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r < nrows) {
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) {
+                        const int64_t prow = GU ? 2 * static_cast<int64_t>(row0 + r) + v
+                                                : static_cast<int64_t>(row0 + r);
+                        wq[r][v] = *reinterpret_cast<const uint4*>(q + prow * rb + static_cast<int64_t>(c) * 16);
+                        if constexpr (AFFINE)
+                            p[r][v] = *reinterpret_cast<const float2*>(sb + 2 * (prow * ng + (k0 >> gshift)));
+                    }
+                }
+            }
+            float dot[R][NV][M];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int m = 0; m < M; ++m) dot[r][v][m] = 0.f;
+            float xs[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) xs[m] = 0.f;
+
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float xv[M][EPD];
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    if (m < m_rows) {
+                        load_vec<XDT, EPD>(xin, static_cast<int64_t>(m) * k + k0 + i * EPD, xv[m]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPD; ++e) xv[m][e] = 0.f;
+                    }
+                    if constexpr (AFFINE) {
+#pragma unroll
+                        for (int e = 0; e < EPD; ++e) xs[m] += xv[m][e];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (r < nrows) {
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) {
+                            const uint32_t w = i == 0 ? wq[r][v].x : i == 1 ? wq[r][v].y
+                                             : i == 2 ? wq[r][v].z : wq[r][v].w;
+                            dot_dword<BITS, M, EPD>(w, xv, dot[r][v]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        if constexpr (AFFINE)
+                            acc[v][r][m] += fmaf(p[r][v].x, dot[r][v][m], p[r][v].y * xs[m]);
+                        else
+                            acc[v][r][m] += dot[r][v][m];
+                    }
+        }
+    }
+
+    __shared__ float part[kWaves][NV][R][M];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float s = wave_sum(acc[v][r][m]);
+                if (lane == 0) part[wave][v][r][m] = s;
+            }
+    __syncthreads();
+
+    const int tid = threadIdx.x;
+    if (tid < R * M) {
+        const int r = tid / M, m = tid % M;
+        if (r < nrows && m < m_rows) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                a0 += part[w][0][r][m];
+                if constexpr (GU) a1 += part[w][NV - 1][r][m];
+            }
+            const int64_t o = static_cast<int64_t>(m) * n_out + row0 + r;
+            if constexpr (GU) {
+                // silu(g) * u with silu(g) = g / (1 + e^-g); the tails give g and -0.
+                const float sg = a0 / (1.0f + expf(-a0));
+                static_cast<float*>(out)[o] = sg * a1;
+            } else {
+                store_elem<ODT>(out, o, load_elem<ODT>(resid, o) + a0);
+            }
+        }
+    }
+}
+
+int gshift_of(int group) { return group == 32 ? 5 : group == 64 ? 6 : group == 128 ? 7 : 0; }
+
+template <int BITS, int XDT, int ODT, int M, bool GU>
+int run(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int m_rows,
+        hipStream_t s) {
+    dim3 grid((n_out + kRows - 1) / kRows), block(64 * kWaves);
+    return static_cast<int>(launch(qgemv_kernel<BITS, XDT, ODT, M, GU>, grid, block, 0, s,
+                                   static_cast<const uint8_t*>(w.q), w.scale_bias, x, r, out, n_out, k,
+                                   gshift_of(w.group), m_rows));
+}
+
+template <int XDT, int ODT, int M, bool GU>
+int run_bits(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k,
+             int m_rows, hipStream_t s) {
+    switch (w.bits) {
+        case 8: return run<8, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s);
+        case 4: return run<4, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s);
+        default: return run<16, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s);
+    }
+}
+
+template <int XDT, int ODT, bool GU>
+int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, void* out,
+             int64_t o_row, int n_out, int k, int m, hipStream_t s) {
+    // rows in blocks of up to 4 (a 1-row kernel for m == 1)
+    if (m == 1) return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s);
+    const size_t xe = XDT == DT_F32 ? 4 : 2;
+    const size_t oe = GU ? 4 : (ODT == DT_F32 ? 4 : 2);
+    for (int m0 = 0; m0 < m; m0 += 4) {
+        const int mr = m - m0 < 4 ? m - m0 : 4;
+        const void* xp = static_cast<const char*>(x) + static_cast<size_t>(m0) * x_row * xe;
+        const void* rp = r ? static_cast<const char*>(r) + static_cast<size_t>(m0) * o_row * oe : nullptr;
+        void* op = static_cast<char*>(out) + static_cast<size_t>(m0) * o_row * oe;
+        const int e = run_bits<XDT, ODT, 4, GU>(w, xp, rp, op, n_out, k, mr, s);
+        if (e) return e;
+    }
+    return 0;
+}
+
+}  // namespace
+
+int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int ffn = gu.n, d = gu.k;
+    switch (act) {
+        case DT_F32: return run_rows<DT_F32, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, s);
+        case DT_F16: return run_rows<DT_F16, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, s);
+        default: return run_rows<DT_BF16, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, s);
+    }
+}
+
+int launch_down_residual(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
+                         void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int d = dn.n, ffn = dn.k;
+    switch (act) {
+        case DT_F32: return run_rows<DT_F32, DT_F32, false>(dn, h, ffn, r, out, d, d, ffn, m, s);
+        case DT_F16: return run_rows<DT_F32, DT_F16, false>(dn, h, ffn, r, out, d, d, ffn, m, s);
+        default: return run_rows<DT_F32, DT_BF16, false>(dn, h, ffn, r, out, d, d, ffn, m, s);
+    }
+}
+
+}  // namespace qdm

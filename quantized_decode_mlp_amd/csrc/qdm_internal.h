@@ -1,0 +1,19 @@
+// Internal interface between the C-ABI layer (qdm_api.cpp, host C++) and the
+// HIP launchers (qdm_*.hip).  Arguments are already validated when these run.
+#pragma once
+
+#include <stdint.h>
+
+#include "qdm.h"
+
+namespace qdm {
+
+// Each returns 0 on success or the hipError_t of the failed launch.
+int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, float* h,
+                          void* stream);
+int launch_down_residual(const float* h, const void* r, int m, int act, const qdm_weight& dn,
+                         void* out, void* stream);
+int launch_add_rmsnorm(const void* a, const void* b, const void* w, int rows, int n, float eps,
+                       int dtype, void* s_out, void* n_out, void* stream);
+
+}  // namespace qdm

@@ -1,0 +1,157 @@
+"""The C-ABI library (CPU): it loads, exports every symbol include/qdm.h
+declares, and rejects bad arguments before launching anything.
+
+Every device-entry-point call here carries at least one invalid argument, so
+validation returns before any HIP call; no compute runs without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_decode_mlp_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qdm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared()
+    assert set(declared) == set(q.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(qdm_[a-z0-9_]+)\b", out))
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+
+
+def test_gfx950_code_object_present():
+    # the offload bundle of this build names its target id
+    data = open(q.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def test_status_strings_and_version():
+    assert q.status_string(0) == "ok"
+    assert "workspace" in q.status_string(q.QDM_ERR_WORKSPACE)
+    assert q.status_string(12345) == "unknown status"
+    assert q.version() >= 100
+
+
+def test_sizes():
+    assert q.packed_q_bytes(4096, 12288, 8) == 4096 * 12288
+    assert q.packed_q_bytes(4096, 14336, 4) == 4096 * 14336 // 2
+    assert q.packed_q_bytes(1536, 8960, 16) == 1536 * 8960 * 2
+    assert q.packed_q_bytes(0, 10, 8) == 0 and q.packed_q_bytes(2, 3, 4) == 0
+    assert q.scale_bias_floats(4096, 12288, 128) == 2 * 4096 * 96
+    assert q.scale_bias_floats(4, 100, 32) == 0
+    assert q.mlp_workspace_bytes(1, 12288) == 12288 * 4
+    assert q.mlp_workspace_bytes(3, 10) == 256
+    assert q.mlp_workspace_bytes(0, 10) == 0
+
+
+L = q._lib
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10004)           # misaligned for 16-byte checks
+
+
+def _w(n=64, k=256, bits=8, group=32, qp=FAKE, sb=FAKE):
+    return q.qdm_weight(n, k, bits, group, qp.value if qp else None, sb.value if sb else None)
+
+
+def _gu(x=FAKE, m=1, act=q.QDM_BF16, w=None, h=FAKE):
+    w = _w() if w is None else w
+    return L.qdm_gemv_gate_up_swiglu(x, m, act, ctypes.byref(w), h, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), q.QDM_ERR_INVALID_ARG),
+    (dict(h=None), q.QDM_ERR_INVALID_ARG),
+    (dict(m=0), q.QDM_ERR_INVALID_ARG),
+    (dict(m=17), q.QDM_ERR_UNSUPPORTED),
+    (dict(act=7), q.QDM_ERR_INVALID_ARG),
+    (dict(w=_w(group=16)), q.QDM_ERR_UNSUPPORTED),
+    (dict(w=_w(k=96, group=64)), q.QDM_ERR_INVALID_ARG),
+    (dict(w=_w(bits=3)), q.QDM_ERR_UNSUPPORTED),
+    (dict(w=_w(bits=16, group=32)), q.QDM_ERR_INVALID_ARG),
+    (dict(w=_w(bits=16, group=0, k=100)), q.QDM_ERR_UNSUPPORTED),
+    (dict(w=_w(sb=None)), q.QDM_ERR_INVALID_ARG),
+    (dict(w=_w(qp=None)), q.QDM_ERR_INVALID_ARG),
+    (dict(w=_w(n=0)), q.QDM_ERR_INVALID_ARG),
+    (dict(w=_w(qp=ODD)), q.QDM_ERR_ALIGNMENT),
+    (dict(w=_w(sb=ctypes.c_void_p(0x10002))), q.QDM_ERR_ALIGNMENT),
+    (dict(x=ODD), q.QDM_ERR_ALIGNMENT),
+    (dict(h=ODD), q.QDM_ERR_ALIGNMENT),
+])
+def test_gate_up_rejects(kw, expect):
+    assert _gu(**kw) == expect
+
+
+def test_down_rejects():
+    w = _w(n=256, k=512)
+    f = lambda h=FAKE, r=FAKE, m=1, act=q.QDM_F32, wt=w, out=ctypes.c_void_p(0x20000): \
+        L.qdm_gemv_down_residual(h, r, m, act, ctypes.byref(wt), out, None)
+    assert f(h=None) == q.QDM_ERR_INVALID_ARG
+    assert f(r=None) == q.QDM_ERR_INVALID_ARG
+    assert f(out=FAKE) == q.QDM_ERR_INVALID_ARG            # out aliases h
+    assert f(m=-1) == q.QDM_ERR_INVALID_ARG
+    assert f(r=ODD) == q.QDM_ERR_ALIGNMENT
+    assert f(wt=_w(n=256, k=500, group=32)) == q.QDM_ERR_INVALID_ARG
+
+
+def test_mlp_rejects():
+    gu = _w(n=512, k=256)
+    dn = _w(n=256, k=512)
+    ws = ctypes.c_void_p(0x30000)
+    out = ctypes.c_void_p(0x40000)
+
+    def f(m=1, gu=gu, dn=dn, ws=ws, wsb=512 * 4, out=out, x=FAKE, r=FAKE):
+        return L.qdm_mlp_decode(x, r, m, q.QDM_F32, ctypes.byref(gu), ctypes.byref(dn), ws, wsb, out, None)
+
+    assert f(wsb=512 * 4 - 1) == q.QDM_ERR_WORKSPACE
+    assert f(ws=None) == q.QDM_ERR_WORKSPACE
+    assert f(m=2, wsb=512 * 4) == q.QDM_ERR_WORKSPACE
+    assert f(dn=_w(n=256, k=1024)) == q.QDM_ERR_INVALID_ARG          # ffn mismatch
+    assert f(dn=_w(n=128, k=512)) == q.QDM_ERR_INVALID_ARG           # d mismatch
+    assert f(dn=_w(n=256, k=512, bits=4)) == q.QDM_ERR_UNSUPPORTED   # mixed formats
+    assert f(out=ws) == q.QDM_ERR_INVALID_ARG
+    assert f(x=None) == q.QDM_ERR_INVALID_ARG
+    assert f(out=ODD) == q.QDM_ERR_ALIGNMENT
+
+
+def test_rmsnorm_rejects():
+    A, B, W, S, N = (ctypes.c_void_p(0x10000 * i) for i in range(1, 6))
+
+    def f(a=A, b=B, w=W, rows=1, n=256, eps=1e-5, dt=q.QDM_F16, s=S, nn=N):
+        return L.qdm_add_rmsnorm(a, b, w, rows, n, eps, dt, s, nn, None)
+
+    assert f(a=None) == q.QDM_ERR_INVALID_ARG
+    assert f(rows=0) == q.QDM_ERR_INVALID_ARG
+    assert f(n=-3) == q.QDM_ERR_INVALID_ARG
+    assert f(eps=float("nan")) == q.QDM_ERR_INVALID_ARG
+    assert f(eps=-1.0) == q.QDM_ERR_INVALID_ARG
+    assert f(dt=5) == q.QDM_ERR_INVALID_ARG
+    assert f(nn=S) == q.QDM_ERR_INVALID_ARG
+    assert f(nn=A) == q.QDM_ERR_INVALID_ARG
+    assert f(w=ODD) == q.QDM_ERR_ALIGNMENT
+
+
+def test_host_pack_rejects():
+    import numpy as np
+    w = np.zeros((4, 64), np.float32)
+    with pytest.raises(q.QdmError) as e:
+        q.quantize_affine(w, 8, 48)
+    assert e.value.status == q.QDM_ERR_UNSUPPORTED
+    w[1, 2] = np.nan
+    with pytest.raises(q.QdmError) as e:
+        q.quantize_pack_rows(w, 8, 32)
+    assert e.value.status == q.QDM_ERR_INVALID_ARG
+    codes = np.full((2, 32), 16, np.uint8)
+    s = np.zeros((2, 1), np.float32)
+    with pytest.raises(q.QdmError):
+        q.pack_rows(codes, s, s, 4, 32)
