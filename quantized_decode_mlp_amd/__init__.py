@@ -49,6 +49,10 @@ class qdm_weight(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime (soname libamdhip64.so.7).  Loading torch
+    # first makes libqdm.so bind to that same runtime instance, so device
+    # pointers and streams from torch are valid in the library's launches.
+    import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
                           "`python -m quantized_decode_mlp_amd.build`")

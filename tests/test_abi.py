@@ -155,3 +155,11 @@ def test_host_pack_rejects():
     s = np.zeros((2, 1), np.float32)
     with pytest.raises(q.QdmError):
         q.pack_rows(codes, s, s, 4, 32)
+
+
+def test_one_hip_runtime_in_process():
+    """libqdm.so binds to the HIP runtime torch loaded, so torch's device
+    pointers and streams are valid in its launches (two runtimes would not
+    share them)."""
+    paths = {l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l}
+    assert len(paths) == 1, paths
