@@ -4,7 +4,7 @@ Argument marshalling only: every step of the hot path runs in the library's
 HIP kernels; PyTorch supplies device memory and the current stream.  The
 names mirror the C ABI in include/qdm.h without the ``qdm_`` prefix.
 
-The library must be built first (``python -m quantized_decode_mlp_amd.build``
+The library must be built first (``python quantized_decode_mlp_amd/build.py``
 or ``__graft_entry__.build()``); importing this package without it raises.
 """
 from __future__ import annotations
@@ -55,7 +55,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
-                          "`python -m quantized_decode_mlp_amd.build`")
+                          "`python quantized_decode_mlp_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     i32, sz, vp, f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
     sig = {

@@ -1,6 +1,7 @@
 """Builds libqdm.so in-tree: host C++ with g++, gfx950 kernels with hipcc.
 
-    python -m quantized_decode_mlp_amd.build
+    python quantized_decode_mlp_amd/build.py      (run by path: importing the
+                                                  package would load the old library)
 
 The host quantizer/packer is compiled with -ffp-contract=off and no
 fast-math (its fp64 steps must stay single IEEE operations).  Kernels are

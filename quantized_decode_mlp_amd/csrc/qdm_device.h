@@ -102,6 +102,34 @@ __device__ __forceinline__ void load_vec(const void* base, int64_t i, float (&ou
     }
 }
 
+// Sum over the 64 lanes of a wave with DPP row steps (xor 1, xor 2, half-row
+// mirror, row mirror) and the four row sums read back from lanes 0/16/32/48;
+// the result is wave-uniform.  Fixed order, so bitwise reproducible.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+    int x = __builtin_bit_cast(int, v);
+    int y;
+    switch (ctrl_sel) {
+        case 0: y = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+        case 1: y = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+        case 2: y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+        default: y = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); break; // row_mirror
+    }
+    return v + __builtin_bit_cast(float, y);
+}
+
+__device__ __forceinline__ float wave_total(float v) {
+    v = dpp_add(v, 0);
+    v = dpp_add(v, 1);
+    v = dpp_add(v, 2);
+    v = dpp_add(v, 3);
+    const int x = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 // Sum over the 64 lanes of a wave; every lane gets the total.  Fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -24,6 +24,7 @@
 
 #include "qdm_device.h"
 #include "qdm_internal.h"
+#include "qdm_launch.h"
 
 namespace qdm {
 namespace {
@@ -183,7 +184,235 @@ qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     }
 }
 
-int gshift_of(int group) { return group == 32 ? 5 : group == 64 ? 6 : group == 128 ? 7 : 0; }
+
+// ---------------------------------------------------------------------------
+// One-row streaming kernel.  Persistent blocks (as many as fit on the chip)
+// walk the output rows in groups of R (R = 1 gate/up pair, or 2 down rows):
+// block b takes groups b, b + gridDim, b + 2*gridDim, ...  A block is S
+// wave64s that split K: wave w owns TW consecutive K-tiles, i.e. chunk
+// c = (w*TW + j)*64 + lane for j < TW, and holds the matching fp32
+// activations (TW*E = 64 values) and their sums in registers for the whole
+// launch.  The next group's weight chunks and scale/bias pairs are loaded
+// (non-temporal: weights are read exactly once) while the current group is
+// reduced, so every wave keeps loads in flight back to back.  Loads are
+// unconditional: a lane past the end of a row or a group past the last row
+// reads a clamped, valid address and its contribution is zeroed through the
+// activations (they are 0 for such lanes) or simply not stored.  Row bases
+// are wave-uniform (scalar registers) and lane offsets 32-bit, so each load
+// is a single global_load with no per-lane 64-bit address arithmetic.  Wave
+// totals come from DPP row reductions; with S > 1 the partials of up to
+// kBatch groups are parked in LDS and combined in wave order after one
+// barrier per batch.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int BITS>
+struct StreamShape {
+    static constexpr int E = 128 / BITS;   // codes per 16-byte chunk
+    static constexpr int TW = 64 / E;      // K-tiles per wave: 64 activations per lane
+};
+
+constexpr int kBatch = 16;   // groups whose split-K partials share one LDS combine
+
+template <int BITS, int XDT, int ODT, bool GU, int S>
+__global__ void __launch_bounds__(64 * S)
+qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
+                    const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
+                    int n_out, int k, int gshift) {
+    constexpr int E = StreamShape<BITS>::E;
+    constexpr int EPD = E / 4;
+    constexpr int TW = StreamShape<BITS>::TW;
+    constexpr int NV = GU ? 2 : 1;
+    constexpr int R = GU ? 1 : 2;
+    constexpr bool AFFINE = BITS != 16;
+
+    const int lane = threadIdx.x & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler keep it scalar
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t rb = static_cast<uint32_t>(k) * BITS / 8;   // bytes per packed row
+    const int C = static_cast<int>(rb >> 4);
+    const uint32_t ng = AFFINE ? static_cast<uint32_t>(k >> gshift) : 0u;
+    const int ngroups = (n_out + R - 1) / R;
+    const int G = static_cast<int>(gridDim.x);
+
+    if (static_cast<int>(blockIdx.x) >= ngroups) return;   // uniform per block, before any barrier
+
+    // lane offsets (bytes) of this wave's chunks, clamped into the row
+    uint32_t qoff[TW], soff[TW];
+    bool vj[TW];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+        const int c = (w * TW + j) * 64 + lane;
+        vj[j] = c < C;
+        const int cc = vj[j] ? c : C - 1;
+        qoff[j] = static_cast<uint32_t>(cc) * 16u;
+        soff[j] = AFFINE ? ((static_cast<uint32_t>(cc) * E) >> gshift) * 8u : 0u;
+    }
+
+    u32x4 wa[R][NV][TW], wb[R][NV][TW];
+    f32x2 pa[R][NV][TW], pb[R][NV][TW];
+
+    auto issue = [&](u32x4 (&wq)[R][NV][TW], f32x2 (&p)[R][NV][TW], int grp) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(grp * R + r, n_out - 1);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t prow = GU ? 2u * static_cast<uint32_t>(row) + v : static_cast<uint32_t>(row);
+                const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
+                const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * ng * 8u;
+#pragma unroll
+                for (int j = 0; j < TW; ++j) {
+                    wq[r][v][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + qoff[j]));
+                    if constexpr (AFFINE)
+                        p[r][v][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + soff[j]));
+                }
+            }
+        }
+    };
+
+    int g = static_cast<int>(blockIdx.x);
+    issue(wa, pa, g);
+
+    float xv[TW][E];
+    float xs[TW];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+        xs[j] = 0.f;
+        const int c = (w * TW + j) * 64 + lane;
+        if (vj[j]) {
+            load_vec<XDT, E>(xin, static_cast<int64_t>(c) * E, xv[j]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) xs[j] += xv[j][e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) xv[j][e] = 0.f;
+        }
+    }
+
+    __shared__ float part[(S > 1) ? kBatch : 1][S][R][NV];
+
+    auto epilogue = [&](int grp, int r, const float (&t)[NV]) {
+        const int row = grp * R + r;
+        if (row < n_out) {
+            if constexpr (GU) {
+                const float gs = t[0];
+                static_cast<float*>(out)[row] = gs / (1.0f + expf(-gs)) * t[NV - 1];
+            } else {
+                store_elem<ODT>(out, row, load_elem<ODT>(resid, row) + t[0]);
+            }
+        }
+    };
+
+    // combines the parked partials of groups first, first+G, ... (cnt of them)
+    auto combine = [&](int first, int cnt) {
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < cnt * R) {
+            const int slot = t / R, r = t % R;
+            float tot[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float a = 0.f;
+#pragma unroll
+                for (int s = 0; s < S; ++s) a += part[slot][s][r][v];
+                tot[v] = a;
+            }
+            epilogue(first + slot * G, r, tot);
+        }
+        __syncthreads();
+    };
+
+    auto finish = [&](const u32x4 (&wq)[R][NV][TW], const f32x2 (&p)[R][NV][TW], int grp, int slot) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float tot[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < TW; ++j) {
+                    float dot = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t word = wq[r][v][j][i];
+#pragma unroll
+                        for (int e = 0; e < EPD; ++e) {
+                            float c;
+                            if constexpr (BITS == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
+                            else if constexpr (BITS == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
+                            else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
+                            dot = fmaf(c, xv[j][i * EPD + e], dot);
+                        }
+                    }
+                    if constexpr (AFFINE) acc += fmaf(p[r][v][j].x, dot, p[r][v][j].y * xs[j]);
+                    else acc += dot;
+                }
+                tot[v] = wave_total(acc);
+            }
+            if constexpr (S == 1) {
+                if (lane == 0) epilogue(grp, r, tot);
+            } else {
+                if (lane == 0) {
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) part[slot][w][r][v] = tot[v];
+                }
+            }
+        }
+    };
+
+    int slot = 0, first = g;
+    while (true) {
+        int gn = g + G;
+        if (gn < ngroups) issue(wb, pb, gn);
+        finish(wa, pa, g, slot);
+        if constexpr (S > 1) {
+            if (++slot == kBatch || gn >= ngroups) { combine(first, slot); slot = 0; first = gn; }
+        }
+        if (gn >= ngroups) break;
+        g = gn;
+        gn = g + G;
+        if (gn < ngroups) issue(wa, pa, gn);
+        finish(wb, pb, g, slot);
+        if constexpr (S > 1) {
+            if (++slot == kBatch || gn >= ngroups) { combine(first, slot); slot = 0; first = gn; }
+        }
+        if (gn >= ngroups) break;
+        g = gn;
+    }
+}
+
+// Waves needed to cover K when each wave holds 64 activations per lane.
+int stream_split(int bits, int k) {
+    const int64_t rb = static_cast<int64_t>(k) * bits / 8;
+    const int64_t tiles = ((rb >> 4) + 63) >> 6;
+    const int tw = bits == 8 ? 4 : bits == 4 ? 2 : 8;
+    return static_cast<int>((tiles + tw - 1) / tw);
+}
+
+template <int BITS, int XDT, int ODT, bool GU, int S>
+int run_stream_s(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s) {
+    auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S>;
+    const int rows_per_group = GU ? 1 : 2;
+    const int groups = (n_out + rows_per_group - 1) / rows_per_group;
+    const int res = resident_blocks(kern, 64 * S, 0);
+    if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
+    const int blocks = groups < res ? groups : res;
+    return static_cast<int>(launch(kern, dim3(blocks), dim3(64 * S), 0, s, static_cast<const uint8_t*>(w.q),
+                                   w.scale_bias, x, r, out, n_out, k, gshift_of(w.group)));
+}
+
+template <int BITS, int XDT, int ODT, bool GU>
+int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s) {
+    switch (stream_split(BITS, k)) {
+        case 1: return run_stream_s<BITS, XDT, ODT, GU, 1>(w, x, r, out, n_out, k, s);
+        case 2: return run_stream_s<BITS, XDT, ODT, GU, 2>(w, x, r, out, n_out, k, s);
+        case 3: return run_stream_s<BITS, XDT, ODT, GU, 3>(w, x, r, out, n_out, k, s);
+        case 4: return run_stream_s<BITS, XDT, ODT, GU, 4>(w, x, r, out, n_out, k, s);
+        case 5: case 6: return run_stream_s<BITS, XDT, ODT, GU, 6>(w, x, r, out, n_out, k, s);
+        default: return run_stream_s<BITS, XDT, ODT, GU, 8>(w, x, r, out, n_out, k, s);
+    }
+}
 
 template <int BITS, int XDT, int ODT, int M, bool GU>
 int run(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int m_rows,
@@ -207,8 +436,18 @@ int run_bits(const qdm_weight& w, const void* x, const void* r, void* out, int n
 template <int XDT, int ODT, bool GU>
 int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, void* out,
              int64_t o_row, int n_out, int k, int m, hipStream_t s) {
-    // rows in blocks of up to 4 (a 1-row kernel for m == 1)
-    if (m == 1) return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s);
+    // one row: the streaming kernel while K fits 8 waves; otherwise (and for
+    // several rows) the block-per-row-group kernel, rows in blocks of up to 4
+    if (m == 1) {
+        if (stream_split(w.bits, k) <= 8) {
+            switch (w.bits) {
+                case 8: return run_stream<8, XDT, ODT, GU>(w, x, r, out, n_out, k, s);
+                case 4: return run_stream<4, XDT, ODT, GU>(w, x, r, out, n_out, k, s);
+                default: return run_stream<16, XDT, ODT, GU>(w, x, r, out, n_out, k, s);
+            }
+        }
+        return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s);
+    }
     const size_t xe = XDT == DT_F32 ? 4 : 2;
     const size_t oe = GU ? 4 : (ODT == DT_F32 ? 4 : 2);
     for (int m0 = 0; m0 < m; m0 += 4) {

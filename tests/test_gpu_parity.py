@@ -262,3 +262,4 @@ def test_add_rmsnorm_in_place_sum():
     s, n = qdm.add_rmsnorm(ad, to_device(b), to_device(w), 1e-5, s_out=ad)
     s_ref, _ = oracle.add_rmsnorm(a.values, b.values, w.values, 1e-5, "f16")
     assert np.array_equal(from_device(ad), s_ref)
+
