@@ -448,6 +448,16 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
         }
         return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s);
     }
+    // 2..16 rows on the matrix cores: bf16 activations for gate/up (exact MMA
+    // operands); for down any 16-bit output (h enters as a bf16 hi/lo split,
+    // ~16 significant bits, so fp32 outputs stay on the vector path)
+    if (mma_rows_supported(w, m)) {
+        if constexpr (GU) {
+            if (XDT == DT_BF16) return launch_gate_up_mma(x, m, w, static_cast<float*>(out), s);
+        } else {
+            if (ODT != DT_F32) return launch_down_mma(static_cast<const float*>(x), r, m, ODT, w, out, s);
+        }
+    }
     const size_t xe = XDT == DT_F32 ? 4 : 2;
     const size_t oe = GU ? 4 : (ODT == DT_F32 ? 4 : 2);
     for (int m0 = 0; m0 < m; m0 += 4) {

@@ -13,6 +13,10 @@ int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, f
                           void* stream);
 int launch_down_residual(const float* h, const void* r, int m, int act, const qdm_weight& dn,
                          void* out, void* stream);
+// Few-row (2..16) projections on the matrix cores (qdm_mfma.hip).
+bool mma_rows_supported(const qdm_weight& w, int m);
+int launch_gate_up_mma(const void* x_bf16, int m, const qdm_weight& gu, float* h, void* stream);
+int launch_down_mma(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, void* stream);
 int launch_add_rmsnorm(const void* a, const void* b, const void* w, int rows, int n, float eps,
                        int dtype, void* s_out, void* n_out, void* stream);
 

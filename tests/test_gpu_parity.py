@@ -129,26 +129,57 @@ def test_shapes_and_dtypes(d, ffn, bits, group, act):
 
 
 @pytest.mark.parametrize("m", [2, 3, 4, 5, 16])
-@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (16, 0)])
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (16, 0), (4, 128)])
 def test_rows(m, bits, group):
-    d, ffn = 320, 448
+    """2..16 rows: bf16 activations take the matrix-core kernels."""
+    d, ffn = 384, 640
     ow, pw = generic_case((m, bits), d, ffn, bits, group)
     x = W.generic_act((m, 4), (m, d), "bf16")
     r = W.generic_act((m, 5), (m, d), "bf16")
     _check_mlp(ow, pw, x, r, TOL["bf16"])
 
 
-def test_rows_match_single_row_calls():
-    """Row i of an m-row call equals the 1-row call on row i (bitwise)."""
-    qdm = _qdm()
+@pytest.mark.parametrize("m", [3, 16])
+@pytest.mark.parametrize("act", ["f16", "f32"])
+@pytest.mark.parametrize("bits,group", [(8, 32), (4, 64)])
+def test_rows_other_dtypes(m, act, bits, group):
+    """f16 activations: vector gate/up, matrix-core down; fp32: vector both."""
     d, ffn = 256, 512
-    _, (gu, dn) = generic_case((77,), d, ffn, 8, 32)
-    x = to_device(W.generic_act((7, 1), (5, d), "bf16"))
-    r = to_device(W.generic_act((7, 2), (5, d), "bf16"))
+    ow, pw = generic_case((m, bits, len(act)), d, ffn, bits, group)
+    x = W.generic_act((m, 6), (m, d), act)
+    r = W.generic_act((m, 7), (m, d), act)
+    _check_mlp(ow, pw, x, r, TOL[act])
+
+
+def test_rows_ragged_tiles_fall_back():
+    """Output widths that are not whole 16-wide tiles use the vector kernel."""
+    d, ffn = 104, 200
+    ow, pw = generic_case((55,), d, ffn, 16, 0)
+    x = W.generic_act((55, 1), (5, d), "bf16")
+    r = W.generic_act((55, 2), (5, d), "bf16")
+    _check_mlp(ow, pw, x, r, TOL["bf16"])
+
+
+@pytest.mark.parametrize("bits,group", [(8, 32), (16, 0)])
+def test_rows_are_independent(bits, group):
+    """Within one m-row call rows do not interact: permuting the input rows
+    permutes the output rows bitwise, and changing one input row changes only
+    that output row."""
+    qdm = _qdm()
+    d, ffn, m = 256, 512, 6
+    _, (gu, dn) = generic_case((77, bits), d, ffn, bits, group)
+    x = to_device(W.generic_act((7, 1), (m, d), "bf16"))
+    r = to_device(W.generic_act((7, 2), (m, d), "bf16"))
     y = qdm.mlp_decode(x, r, gu, dn)
-    for i in range(5):
-        yi = qdm.mlp_decode(x[i:i + 1].contiguous(), r[i:i + 1].contiguous(), gu, dn)
-        assert torch.equal(yi[0], y[i])
+    p = torch.tensor([3, 0, 5, 1, 4, 2], device="cuda")
+    yp = qdm.mlp_decode(x[p].contiguous(), r[p].contiguous(), gu, dn)
+    assert torch.equal(yp, y[p])
+    x2 = x.clone()
+    x2[4] = -x2[4]
+    y2 = qdm.mlp_decode(x2, r, gu, dn)
+    keep = [0, 1, 2, 3, 5]
+    assert torch.equal(y2[keep], y[keep])
+    assert not torch.equal(y2[4], y[4])
 
 
 # ------------------------------------------------------------------ special cases (bitwise)
