@@ -187,101 +187,187 @@ qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 
 // ---------------------------------------------------------------------------
 // One-row streaming kernel.  Persistent blocks (as many as fit on the chip)
-// walk the output rows in groups of R (R = 1 gate/up pair, or 2 down rows):
-// block b takes groups b, b + gridDim, b + 2*gridDim, ...  A block is S
-// wave64s that split K: wave w owns TW consecutive K-tiles, i.e. chunk
-// c = (w*TW + j)*64 + lane for j < TW, and holds the matching fp32
-// activations (TW*E = 64 values) and their sums in registers for the whole
-// launch.  The next group's weight chunks and scale/bias pairs are loaded
-// (non-temporal: weights are read exactly once) while the current group is
-// reduced, so every wave keeps loads in flight back to back.  Loads are
-// unconditional: a lane past the end of a row or a group past the last row
+// walk the outputs (a gate/up pair, or one down row) in rounds.  A block is P
+// independent row streams of S wave64s each; the S waves of a stream split
+// K: wave ks owns TW consecutive K-tiles, i.e. chunk c = (ks*TW + j)*64 +
+// lane for j < TW, and holds the matching fp32 activations (TW*E of them, at
+// most 64) and their sums in registers for the whole launch.
+//
+// For the down projection, whose fp32 activations outweigh the weight bytes
+// that use them (4 bytes per 8-bit code), the row is copied once per block
+// into LDS (each thread moves a few 16-byte pieces) and every wave
+// reads its slice from there: one copy per block instead of one per wave
+// through the vector-memory path, which a CU shares between all of its
+// waves.  For gate/up (16-bit x shared by the pair's two rows) each wave
+// loads its slice directly and a block is a single stream.
+//
+// Each round a wave loads its TW weight chunks of the round's row(s)
+// (non-temporal: weights are read exactly once) while it reduces the
+// previous round's.  Scale/bias pairs are loaded compactly: the pairs of a
+// wave's K-range (TW*64*E/G of them per row; gate and up pairs sit side by
+// side) come in with one 8-byte load per lane, and each lane fetches the
+// pair of its own group from the owning lane with ds_bpermute.  Loads are
+// unconditional: a lane past the end of a row or a stream past its last row
 // reads a clamped, valid address and its contribution is zeroed through the
-// activations (they are 0 for such lanes) or simply not stored.  Row bases
-// are wave-uniform (scalar registers) and lane offsets 32-bit, so each load
-// is a single global_load with no per-lane 64-bit address arithmetic.  Wave
-// totals come from DPP row reductions; with S > 1 the partials of up to
-// kBatch groups are parked in LDS and combined in wave order after one
-// barrier per batch.
+// activations (0 for such lanes) or not stored.  Row bases are wave-uniform
+// (scalar registers) and lane offsets 32-bit.  Wave totals come from DPP row
+// reductions; the split-K partials of up to kBatch rounds are parked in LDS
+// and combined in wave order after one barrier per batch, so results are
+// bitwise reproducible.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int BITS>
 struct StreamShape {
-    static constexpr int E = 128 / BITS;   // codes per 16-byte chunk
-    static constexpr int TW = 64 / E;      // K-tiles per wave: 64 activations per lane
+    static constexpr int E = 128 / BITS;                              // codes per 16-byte chunk
+    static constexpr int LOGE = BITS == 8 ? 4 : BITS == 4 ? 5 : 3;   // log2(E)
+    static constexpr int TW_MAX = 64 / E;                             // K-tiles per wave at most
 };
 
-constexpr int kBatch = 16;   // groups whose split-K partials share one LDS combine
+constexpr int kBatch = 16;            // rounds whose split-K partials share one LDS combine
+constexpr int kStreamLds = 65536;     // largest activation row staged in LDS (bytes)
 
-template <int BITS, int XDT, int ODT, bool GU, int S>
-__global__ void __launch_bounds__(64 * S)
+template <int XDT>
+constexpr int x_bytes() { return XDT == DT_F32 ? 4 : 2; }
+
+// Stream (block b, p) takes groups b*P + p + i*G*P for rounds i = 0, 1, ...
+// (G = gridDim); every wave walks the same number of rounds, so the block's
+// barriers line up even when a stream has run out of groups.
+template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P, int NB, bool XL>
+__global__ void __launch_bounds__(64 * S * P)
 qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                     const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
                     int n_out, int k, int gshift) {
     constexpr int E = StreamShape<BITS>::E;
     constexpr int EPD = E / 4;
-    constexpr int TW = StreamShape<BITS>::TW;
     constexpr int NV = GU ? 2 : 1;
-    constexpr int R = GU ? 1 : 2;
     constexpr bool AFFINE = BITS != 16;
+    constexpr int NT = 64 * S * P;
+    // pair loads per round: a wave's K-range holds at most TW*64*E/32 pairs per row
+    constexpr int NL = AFFINE ? (NV * TW * 2 * E + 63) / 64 : 1;
+    constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
+
+    // XL: activations reach the registers through an LDS copy of the row that
+    // the whole block shares, instead of straight from global memory
+    extern __shared__ __align__(16) uint8_t xlds[];   // the activation row, k * x_bytes bytes
+    __shared__ float part[(S > 1) ? kBatch : 1][P][S][NV];
 
     const int lane = threadIdx.x & 63;
     // wave-uniform by construction; readfirstlane lets the compiler keep it scalar
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wv % S, p = wv / S;
     const uint32_t rb = static_cast<uint32_t>(k) * BITS / 8;   // bytes per packed row
     const int C = static_cast<int>(rb >> 4);
-    const uint32_t ng = AFFINE ? static_cast<uint32_t>(k >> gshift) : 0u;
-    const int ngroups = (n_out + R - 1) / R;
-    const int G = static_cast<int>(gridDim.x);
+    const int ng = AFFINE ? (k >> gshift) : 0;
+    const int GP = static_cast<int>(gridDim.x) * P;
+    const int g0 = static_cast<int>(blockIdx.x) * P + p;
+    const int rounds = (n_out - static_cast<int>(blockIdx.x) * P + GP - 1) / GP;   // same for every wave
+    if (rounds <= 0) return;   // uniform per block, before any barrier
 
-    if (static_cast<int>(blockIdx.x) >= ngroups) return;   // uniform per block, before any barrier
+    // first pieces of the activation row (issued before the weights: the
+    // in-order load counter then lets them land without waiting for weights)
+    const int nunits = (k * x_bytes<XDT>()) >> 4;
+    const u32x4* xg = static_cast<const u32x4*>(xin);
+    u32x4* xl = reinterpret_cast<u32x4*>(xlds);
+    u32x4 xt[XU];
+    if constexpr (XL) {
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int idx = static_cast<int>(threadIdx.x) + u * NT;
+            if (idx < nunits) xt[u] = xg[idx];
+        }
+    }
 
     // lane offsets (bytes) of this wave's chunks, clamped into the row
-    uint32_t qoff[TW], soff[TW];
+    uint32_t qoff[TW];
     bool vj[TW];
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
-        const int c = (w * TW + j) * 64 + lane;
+        const int c = (ks * TW + j) * 64 + lane;
         vj[j] = c < C;
-        const int cc = vj[j] ? c : C - 1;
-        qoff[j] = static_cast<uint32_t>(cc) * 16u;
-        soff[j] = AFFINE ? ((static_cast<uint32_t>(cc) * E) >> gshift) * 8u : 0u;
+        qoff[j] = static_cast<uint32_t>(vj[j] ? c : C - 1) * 16u;
     }
 
-    u32x4 wa[R][NV][TW], wb[R][NV][TW];
-    f32x2 pa[R][NV][TW], pb[R][NV][TW];
-
-    auto issue = [&](u32x4 (&wq)[R][NV][TW], f32x2 (&p)[R][NV][TW], int grp) {
+    // Pair layout.  PPC = 64*E/G pairs per K-tile, npr = TW*PPC per row.
+    // Load i, lane m reads entry t = 64*i + m of [row-0 pairs | row-1 pairs]
+    // (row 1: the up half of a gate/up pair), clamped into the row.  Chunk j
+    // of row v needs entry v*npr + j*PPC + lane/(G/E): a PPC-aligned run that
+    // never straddles two loads, so the load index is wave-uniform.
+    uint32_t poff[NL];
+    int psel[NV][TW], bpa[NV][TW];
+    int nl = 0;
+    if constexpr (AFFINE) {
+        const int lpg = gshift - StreamShape<BITS>::LOGE;   // log2(lanes per group)
+        const int ppc_log = 6 - lpg;
+        const int npr = TW << ppc_log;
+        nl = (NV * npr + 63) >> 6;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = min(grp * R + r, n_out - 1);
+        for (int i = 0; i < NL; ++i) {
+            const int t = 64 * i + lane;
+            const int v = min(t / npr, NV - 1);
+            const int tp = min(t - v * npr, npr - 1);
+            poff[i] = static_cast<uint32_t>(v * ng + min(ks * npr + tp, ng - 1)) * 8u;
+        }
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const uint32_t prow = GU ? 2u * static_cast<uint32_t>(row) + v : static_cast<uint32_t>(row);
-                const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
-                const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * ng * 8u;
+        for (int v = 0; v < NV; ++v) {
 #pragma unroll
-                for (int j = 0; j < TW; ++j) {
-                    wq[r][v][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + qoff[j]));
-                    if constexpr (AFFINE)
-                        p[r][v][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + soff[j]));
-                }
+            for (int j = 0; j < TW; ++j) {
+                const int u = v * npr + (j << ppc_log) + (lane >> lpg);
+                psel[v][j] = __builtin_amdgcn_readfirstlane(u >> 6);
+                bpa[v][j] = (u & 63) << 2;
             }
+        }
+    }
+
+    u32x4 wbuf[NB][NV][TW];
+    f32x2 pbuf[NB][NL];
+
+    // loads of group grp (rows clamped; a stream past its last group reloads row n_out - 1)
+    auto issue = [&](u32x4 (&wq)[NV][TW], f32x2 (&pp)[NL], int grp) {
+        const uint32_t row = static_cast<uint32_t>(min(grp, n_out - 1));
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const uint32_t prow = GU ? 2u * row + v : row;
+            const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
+#pragma unroll
+            for (int j = 0; j < TW; ++j)
+                wq[v][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + qoff[j]));
+        }
+        if constexpr (AFFINE) {
+            const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) +
+                                  static_cast<size_t>(GU ? 2u * row : row) * static_cast<uint32_t>(ng) * 8u;
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                if (i == 0 || i < nl)
+                    pp[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + poff[i]));
         }
     };
 
-    int g = static_cast<int>(blockIdx.x);
-    issue(wa, pa, g);
+    // the first NB - 1 rounds go in flight
+#pragma unroll
+    for (int b = 0; b < NB - 1; ++b)
+        if (g0 + b * GP < n_out) issue(wbuf[b], pbuf[b], g0 + b * GP);
+
+    // rest of the activation copy, then this wave's slice
+    if constexpr (XL) {
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int idx = static_cast<int>(threadIdx.x) + u * NT;
+            if (idx < nunits) xl[idx] = xt[u];
+        }
+        for (int idx = static_cast<int>(threadIdx.x) + XU * NT; idx < nunits; idx += NT) xl[idx] = xg[idx];
+        __syncthreads();
+    }
 
     float xv[TW][E];
     float xs[TW];
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
         xs[j] = 0.f;
-        const int c = (w * TW + j) * 64 + lane;
+        const int c = (ks * TW + j) * 64 + lane;
         if (vj[j]) {
-            load_vec<XDT, E>(xin, static_cast<int64_t>(c) * E, xv[j]);
+            if constexpr (XL) load_vec<XDT, E>(xlds, static_cast<int64_t>(c) * E, xv[j]);
+            else load_vec<XDT, E>(xin, static_cast<int64_t>(c) * E, xv[j]);
 #pragma unroll
             for (int e = 0; e < E; ++e) xs[j] += xv[j][e];
         } else {
@@ -290,127 +376,188 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         }
     }
 
-    __shared__ float part[(S > 1) ? kBatch : 1][S][R][NV];
-
-    auto epilogue = [&](int grp, int r, const float (&t)[NV]) {
-        const int row = grp * R + r;
-        if (row < n_out) {
-            if constexpr (GU) {
-                const float gs = t[0];
-                static_cast<float*>(out)[row] = gs / (1.0f + expf(-gs)) * t[NV - 1];
-            } else {
-                store_elem<ODT>(out, row, load_elem<ODT>(resid, row) + t[0]);
-            }
+    auto epilogue = [&](int grp, const float (&t)[NV]) {
+        if constexpr (GU) {
+            const float gs = t[0];
+            static_cast<float*>(out)[grp] = gs / (1.0f + expf(-gs)) * t[NV - 1];
+        } else {
+            store_elem<ODT>(out, grp, load_elem<ODT>(resid, grp) + t[0]);
         }
     };
 
-    // combines the parked partials of groups first, first+G, ... (cnt of them)
+    // combines the parked partials of rounds first .. first+cnt-1 for every stream
     auto combine = [&](int first, int cnt) {
         __syncthreads();
         const int t = threadIdx.x;
-        if (t < cnt * R) {
-            const int slot = t / R, r = t % R;
-            float tot[NV];
+        if (t < cnt * P) {
+            const int slot = t / P, sp = t % P;
+            const int grp = static_cast<int>(blockIdx.x) * P + sp + (first + slot) * GP;
+            if (grp < n_out) {
+                float tot[NV];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                float a = 0.f;
+                for (int v = 0; v < NV; ++v) {
+                    float a = 0.f;
 #pragma unroll
-                for (int s = 0; s < S; ++s) a += part[slot][s][r][v];
-                tot[v] = a;
+                    for (int s2 = 0; s2 < S; ++s2) a += part[slot][sp][s2][v];
+                    tot[v] = a;
+                }
+                epilogue(grp, tot);
             }
-            epilogue(first + slot * G, r, tot);
         }
         __syncthreads();
     };
 
-    auto finish = [&](const u32x4 (&wq)[R][NV][TW], const f32x2 (&p)[R][NV][TW], int grp, int slot) {
+    auto finish = [&](const u32x4 (&wq)[NV][TW], const f32x2 (&pp)[NL], int grp, int slot) {
+        if (grp >= n_out) return;   // this stream is past its last group (wave-uniform)
+        float tot[NV];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float tot[NV];
+        for (int v = 0; v < NV; ++v) {
+            float acc = 0.f;
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                float acc = 0.f;
+            for (int j = 0; j < TW; ++j) {
+                float dot = 0.f;
 #pragma unroll
-                for (int j = 0; j < TW; ++j) {
-                    float dot = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t word = wq[v][j][i];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t word = wq[r][v][j][i];
-#pragma unroll
-                        for (int e = 0; e < EPD; ++e) {
-                            float c;
-                            if constexpr (BITS == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
-                            else if constexpr (BITS == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
-                            else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
-                            dot = fmaf(c, xv[j][i * EPD + e], dot);
-                        }
+                    for (int e = 0; e < EPD; ++e) {
+                        float c;
+                        if constexpr (BITS == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
+                        else if constexpr (BITS == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
+                        else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
+                        dot = fmaf(c, xv[j][i * EPD + e], dot);
                     }
-                    if constexpr (AFFINE) acc += fmaf(p[r][v][j].x, dot, p[r][v][j].y * xs[j]);
-                    else acc += dot;
                 }
-                tot[v] = wave_total(acc);
-            }
-            if constexpr (S == 1) {
-                if (lane == 0) epilogue(grp, r, tot);
-            } else {
-                if (lane == 0) {
+                if constexpr (AFFINE) {
+                    f32x2 pv = pp[0];
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) part[slot][w][r][v] = tot[v];
+                    for (int i = 1; i < NL; ++i)
+                        if (psel[v][j] == i) pv = pp[i];
+                    const float sc = __int_as_float(__builtin_amdgcn_ds_bpermute(bpa[v][j], __float_as_int(pv.x)));
+                    const float bi = __int_as_float(__builtin_amdgcn_ds_bpermute(bpa[v][j], __float_as_int(pv.y)));
+                    acc += fmaf(sc, dot, bi * xs[j]);
+                } else {
+                    acc += dot;
                 }
+            }
+            tot[v] = wave_total(acc);
+        }
+        if constexpr (S == 1) {
+            if (lane == 0) epilogue(grp, tot);
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) part[slot][p][ks][v] = tot[v];
             }
         }
     };
 
-    int slot = 0, first = g;
-    while (true) {
-        int gn = g + G;
-        if (gn < ngroups) issue(wb, pb, gn);
-        finish(wa, pa, g, slot);
-        if constexpr (S > 1) {
-            if (++slot == kBatch || gn >= ngroups) { combine(first, slot); slot = 0; first = gn; }
+    // round i lives in buffer i % NB; round i + NB - 1 is issued before round i is reduced
+    int slot = 0, first = 0;
+    for (int i0 = 0; i0 < rounds; i0 += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int i = i0 + b;
+            if (i < rounds) {   // uniform per block
+                const int gi = g0 + (i + NB - 1) * GP;
+                if (gi < n_out) issue(wbuf[(b + NB - 1) % NB], pbuf[(b + NB - 1) % NB], gi);
+                finish(wbuf[b], pbuf[b], g0 + i * GP, slot);
+                if constexpr (S > 1) {
+                    if (++slot == kBatch || i + 1 == rounds) { combine(first, slot); slot = 0; first = i + 1; }
+                }
+            }
         }
-        if (gn >= ngroups) break;
-        g = gn;
-        gn = g + G;
-        if (gn < ngroups) issue(wa, pa, gn);
-        finish(wb, pb, g, slot);
-        if constexpr (S > 1) {
-            if (++slot == kBatch || gn >= ngroups) { combine(first, slot); slot = 0; first = gn; }
-        }
-        if (gn >= ngroups) break;
-        g = gn;
     }
 }
 
-// Waves needed to cover K when each wave holds 64 activations per lane.
-int stream_split(int bits, int k) {
+// Whether the streaming kernel stages the activation row in LDS: for the down
+// projection, whose fp32 h outweighs the weight bytes that use it (2 to 8
+// times); not for gate/up, whose 16-bit x is shared by the pair's two rows.
+constexpr bool stream_stages_x(bool gu) { return !gu; }
+
+// K split of the streaming kernel for rows of k codes (t 1-KiB K-tiles).
+// Staged activations: two tiles per wave where t splits evenly into at most 8
+// such waves, else one tile per wave for t <= 8.  Activations from global
+// memory: one tile per wave for t <= 8.  Beyond: 8 waves of up to the per-wave
+// register limit.  Returns false when K needs more, or when a staged
+// activation row (xb bytes per element) does not fit in LDS.
+struct StreamSplit { int s, tw; };
+
+bool stream_split(int bits, int k, int xb, bool stage, StreamSplit& out) {
+    if (stage && static_cast<int64_t>(k) * xb > kStreamLds) return false;
     const int64_t rb = static_cast<int64_t>(k) * bits / 8;
-    const int64_t tiles = ((rb >> 4) + 63) >> 6;
-    const int tw = bits == 8 ? 4 : bits == 4 ? 2 : 8;
-    return static_cast<int>((tiles + tw - 1) / tw);
+    const int t = static_cast<int>(((rb >> 4) + 63) >> 6);
+    const int tw_max = bits == 8 ? 4 : bits == 4 ? 2 : 8;
+    if (stage && t % 2 == 0 && t <= 16) { out = {t / 2, 2}; return true; }
+    if (t <= 8) { out = {t, 1}; return true; }
+    const int tw = (t + 7) / 8;
+    if (tw <= tw_max) { out = {8, tw}; return true; }
+    return false;
+}
+
+// Row streams per block: as many as fit in 16 waves while the registers one
+// wave needs (estimated from its double-buffered weight chunks and its slice
+// of activations) stay within what that block size leaves per wave.
+constexpr int stream_rows_per_block(int bits, bool gu, int s, int tw) {
+    const int e = 128 / bits;
+    const int est = (gu ? 2 : 1) * tw * (bits == 16 ? 8 : 12) + tw * (e + 1) + 30;
+    const int waves = est <= 128 ? 16 : est <= 256 ? 8 : 4;
+    return waves / s > 0 ? waves / s : 1;
+}
+
+template <int BITS, int XDT, int ODT, bool GU, int S, int TW>
+int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s) {
+    if constexpr (TW > StreamShape<BITS>::TW_MAX) {
+        return static_cast<int>(hipErrorInvalidValue);
+    } else {
+        constexpr bool STAGE = stream_stages_x(GU);
+        constexpr int P = STAGE ? stream_rows_per_block(BITS, GU, S, TW) : 1;
+        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, 2, STAGE>;
+        const size_t lds = STAGE ? static_cast<size_t>(k) * x_bytes<XDT>() : 0;
+        const int res = resident_blocks(kern, 64 * S * P, lds);
+        if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
+        const int need = (n_out + P - 1) / P;
+        const int blocks = need < res ? need : res;
+        return static_cast<int>(launch(kern, dim3(blocks), dim3(64 * S * P), lds, s,
+                                       static_cast<const uint8_t*>(w.q), w.scale_bias, x, r, out, n_out, k,
+                                       gshift_of(w.group)));
+    }
 }
 
 template <int BITS, int XDT, int ODT, bool GU, int S>
-int run_stream_s(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s) {
-    auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S>;
-    const int rows_per_group = GU ? 1 : 2;
-    const int groups = (n_out + rows_per_group - 1) / rows_per_group;
-    const int res = resident_blocks(kern, 64 * S, 0);
-    if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
-    const int blocks = groups < res ? groups : res;
-    return static_cast<int>(launch(kern, dim3(blocks), dim3(64 * S), 0, s, static_cast<const uint8_t*>(w.q),
-                                   w.scale_bias, x, r, out, n_out, k, gshift_of(w.group)));
+int run_stream_s(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
+                 hipStream_t s) {
+    switch (tw) {
+        case 1: return run_stream_st<BITS, XDT, ODT, GU, S, 1>(w, x, r, out, n_out, k, s);
+        case 2: return run_stream_st<BITS, XDT, ODT, GU, S, 2>(w, x, r, out, n_out, k, s);
+        case 3: return run_stream_st<BITS, XDT, ODT, GU, S, 3>(w, x, r, out, n_out, k, s);
+        case 4: return run_stream_st<BITS, XDT, ODT, GU, S, 4>(w, x, r, out, n_out, k, s);
+        case 5: return run_stream_st<BITS, XDT, ODT, GU, S, 5>(w, x, r, out, n_out, k, s);
+        case 6: return run_stream_st<BITS, XDT, ODT, GU, S, 6>(w, x, r, out, n_out, k, s);
+        case 7: return run_stream_st<BITS, XDT, ODT, GU, S, 7>(w, x, r, out, n_out, k, s);
+        default: return run_stream_st<BITS, XDT, ODT, GU, S, 8>(w, x, r, out, n_out, k, s);
+    }
+}
+
+template <int BITS, int XDT, int ODT, bool GU, int S>
+int run_stream_s12(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
+                   hipStream_t s) {
+    return tw == 1 ? run_stream_st<BITS, XDT, ODT, GU, S, 1>(w, x, r, out, n_out, k, s)
+                   : run_stream_st<BITS, XDT, ODT, GU, S, 2>(w, x, r, out, n_out, k, s);
 }
 
 template <int BITS, int XDT, int ODT, bool GU>
-int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s) {
-    switch (stream_split(BITS, k)) {
-        case 1: return run_stream_s<BITS, XDT, ODT, GU, 1>(w, x, r, out, n_out, k, s);
-        case 2: return run_stream_s<BITS, XDT, ODT, GU, 2>(w, x, r, out, n_out, k, s);
-        case 3: return run_stream_s<BITS, XDT, ODT, GU, 3>(w, x, r, out, n_out, k, s);
-        case 4: return run_stream_s<BITS, XDT, ODT, GU, 4>(w, x, r, out, n_out, k, s);
-        case 5: case 6: return run_stream_s<BITS, XDT, ODT, GU, 6>(w, x, r, out, n_out, k, s);
-        default: return run_stream_s<BITS, XDT, ODT, GU, 8>(w, x, r, out, n_out, k, s);
+int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, const StreamSplit& sp,
+               hipStream_t s) {
+    switch (sp.s) {
+        case 1: return run_stream_s12<BITS, XDT, ODT, GU, 1>(w, x, r, out, n_out, k, sp.tw, s);
+        case 2: return run_stream_s12<BITS, XDT, ODT, GU, 2>(w, x, r, out, n_out, k, sp.tw, s);
+        case 3: return run_stream_s12<BITS, XDT, ODT, GU, 3>(w, x, r, out, n_out, k, sp.tw, s);
+        case 4: return run_stream_s12<BITS, XDT, ODT, GU, 4>(w, x, r, out, n_out, k, sp.tw, s);
+        case 5: return run_stream_s12<BITS, XDT, ODT, GU, 5>(w, x, r, out, n_out, k, sp.tw, s);
+        case 6: return run_stream_s12<BITS, XDT, ODT, GU, 6>(w, x, r, out, n_out, k, sp.tw, s);
+        case 7: return run_stream_s12<BITS, XDT, ODT, GU, 7>(w, x, r, out, n_out, k, sp.tw, s);
+        default: return run_stream_s<BITS, XDT, ODT, GU, 8>(w, x, r, out, n_out, k, sp.tw, s);
     }
 }
 
@@ -436,14 +583,15 @@ int run_bits(const qdm_weight& w, const void* x, const void* r, void* out, int n
 template <int XDT, int ODT, bool GU>
 int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, void* out,
              int64_t o_row, int n_out, int k, int m, hipStream_t s) {
-    // one row: the streaming kernel while K fits 8 waves; otherwise (and for
+    // one row: the streaming kernel while K fits 8 waves of 64 activations; otherwise (and for
     // several rows) the block-per-row-group kernel, rows in blocks of up to 4
     if (m == 1) {
-        if (stream_split(w.bits, k) <= 8) {
+        StreamSplit sp;
+        if (stream_split(w.bits, k, x_bytes<XDT>(), stream_stages_x(GU), sp)) {
             switch (w.bits) {
-                case 8: return run_stream<8, XDT, ODT, GU>(w, x, r, out, n_out, k, s);
-                case 4: return run_stream<4, XDT, ODT, GU>(w, x, r, out, n_out, k, s);
-                default: return run_stream<16, XDT, ODT, GU>(w, x, r, out, n_out, k, s);
+                case 8: return run_stream<8, XDT, ODT, GU>(w, x, r, out, n_out, k, sp, s);
+                case 4: return run_stream<4, XDT, ODT, GU>(w, x, r, out, n_out, k, sp, s);
+                default: return run_stream<16, XDT, ODT, GU>(w, x, r, out, n_out, k, sp, s);
             }
         }
         return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s);
