@@ -201,13 +201,12 @@ qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 // waves.  For gate/up (16-bit x shared by the pair's two rows) each wave
 // loads its slice directly and a block is a single stream.
 //
-// Each round a wave loads its TW weight chunks of the round's row(s)
-// (non-temporal: weights are read exactly once) while it reduces the
-// previous round's.  Scale/bias pairs are loaded compactly: the pairs of a
-// wave's K-range (TW*64*E/G of them per row; gate and up pairs sit side by
-// side) come in with one 8-byte load per lane, and each lane fetches the
-// pair of its own group from the owning lane with ds_bpermute.  Loads are
-// unconditional: a lane past the end of a row or a stream past its last row
+// Each round a wave loads its TW weight chunks of the round's row(s) and
+// the scale/bias pair of each chunk's group (non-temporal: weights are read
+// exactly once) while it reduces the previous round's.  (Loading a wave's
+// pairs once and spreading them with ds_bpermute costs fewer load
+// instructions but puts an LDS round trip on every round's critical path;
+// measured slower.)  Loads are unconditional: a lane past the end of a row or a stream past its last row
 // reads a clamped, valid address and its contribution is zeroed through the
 // activations (0 for such lanes) or not stored.  Row bases are wave-uniform
 // (scalar registers) and lane offsets 32-bit.  Wave totals come from DPP row
@@ -216,11 +215,12 @@ qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 // bitwise reproducible.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
 
 template <int BITS>
 struct StreamShape {
     static constexpr int E = 128 / BITS;                              // codes per 16-byte chunk
-    static constexpr int LOGE = BITS == 8 ? 4 : BITS == 4 ? 5 : 3;   // log2(E)
     static constexpr int TW_MAX = 64 / E;                             // K-tiles per wave at most
 };
 
@@ -243,8 +243,6 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     constexpr int NV = GU ? 2 : 1;
     constexpr bool AFFINE = BITS != 16;
     constexpr int NT = 64 * S * P;
-    // pair loads per round: a wave's K-range holds at most TW*64*E/32 pairs per row
-    constexpr int NL = AFFINE ? (NV * TW * 2 * E + 63) / 64 : 1;
     constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
 
     // XL: activations reach the registers through an LDS copy of the row that
@@ -278,68 +276,36 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         }
     }
 
-    // lane offsets (bytes) of this wave's chunks, clamped into the row
-    uint32_t qoff[TW];
+    // lane offsets (bytes) of this wave's chunks and of their scale/bias pairs,
+    // clamped into the row
+    uint32_t qoff[TW], soff[TW];
     bool vj[TW];
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
         const int c = (ks * TW + j) * 64 + lane;
         vj[j] = c < C;
-        qoff[j] = static_cast<uint32_t>(vj[j] ? c : C - 1) * 16u;
-    }
-
-    // Pair layout.  PPC = 64*E/G pairs per K-tile, npr = TW*PPC per row.
-    // Load i, lane m reads entry t = 64*i + m of [row-0 pairs | row-1 pairs]
-    // (row 1: the up half of a gate/up pair), clamped into the row.  Chunk j
-    // of row v needs entry v*npr + j*PPC + lane/(G/E): a PPC-aligned run that
-    // never straddles two loads, so the load index is wave-uniform.
-    uint32_t poff[NL];
-    int psel[NV][TW], bpa[NV][TW];
-    int nl = 0;
-    if constexpr (AFFINE) {
-        const int lpg = gshift - StreamShape<BITS>::LOGE;   // log2(lanes per group)
-        const int ppc_log = 6 - lpg;
-        const int npr = TW << ppc_log;
-        nl = (NV * npr + 63) >> 6;
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int t = 64 * i + lane;
-            const int v = min(t / npr, NV - 1);
-            const int tp = min(t - v * npr, npr - 1);
-            poff[i] = static_cast<uint32_t>(v * ng + min(ks * npr + tp, ng - 1)) * 8u;
-        }
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-#pragma unroll
-            for (int j = 0; j < TW; ++j) {
-                const int u = v * npr + (j << ppc_log) + (lane >> lpg);
-                psel[v][j] = __builtin_amdgcn_readfirstlane(u >> 6);
-                bpa[v][j] = (u & 63) << 2;
-            }
-        }
+        const uint32_t cc = static_cast<uint32_t>(vj[j] ? c : C - 1);
+        qoff[j] = cc * 16u;
+        soff[j] = AFFINE ? ((cc * E) >> gshift) * 8u : 0u;
     }
 
     u32x4 wbuf[NB][NV][TW];
-    f32x2 pbuf[NB][NL];
+    f32x2 pbuf[NB][NV][TW];
 
     // loads of group grp (rows clamped; a stream past its last group reloads row n_out - 1)
-    auto issue = [&](u32x4 (&wq)[NV][TW], f32x2 (&pp)[NL], int grp) {
+    auto issue = [&](u32x4 (&wq)[NV][TW], f32x2 (&pp)[NV][TW], int grp) {
         const uint32_t row = static_cast<uint32_t>(min(grp, n_out - 1));
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const uint32_t prow = GU ? 2u * row + v : row;
             const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
+            const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * ng * 8u;
 #pragma unroll
-            for (int j = 0; j < TW; ++j)
+            for (int j = 0; j < TW; ++j) {
                 wq[v][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + qoff[j]));
-        }
-        if constexpr (AFFINE) {
-            const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) +
-                                  static_cast<size_t>(GU ? 2u * row : row) * static_cast<uint32_t>(ng) * 8u;
-#pragma unroll
-            for (int i = 0; i < NL; ++i)
-                if (i == 0 || i < nl)
-                    pp[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + poff[i]));
+                if constexpr (AFFINE)
+                    pp[v][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + soff[j]));
+            }
         }
     };
 
@@ -359,6 +325,21 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         __syncthreads();
     }
 
+    // Dot-product form.  DM 0: fp32 activations, one FMA per code.  DM 1
+    // (8/4-bit codes, 16-bit activations): v_dot2_f32_f16 on two codes at a
+    // time.  A code becomes an exact f16 value by placing its bits in the
+    // mantissa under a fixed exponent: an 8-bit code c under the exponent
+    // byte 0x64 gives 1024 + c (one byte permute per two codes); a 4-bit
+    // code n in the top mantissa bits of 1.0 gives 1 + n/16 (a shift and an
+    // and-or per two codes), which keeps the offset small against the code.
+    // The activations are held as f16 after a per-wave power-of-two scale
+    // 2^sg that puts the slice maximum in [2^14, 2^15) (a bf16 or f16 value
+    // converts exactly unless it lies more than 2^28 below that maximum); the
+    // offset's share (1024 or 1 times the chunk's scaled activation sum) is
+    // taken off per chunk before the group scale applies, and the powers of
+    // two come off once per row.  DM 2 (bf16 weights, bf16 activations):
+    // v_dot2_f32_bf16 straight on the packed words.
+    constexpr int DM = (AFFINE && XDT != DT_F32) ? 1 : (BITS == 16 && XDT == DT_BF16) ? 2 : 0;
     float xv[TW][E];
     float xs[TW];
 #pragma unroll
@@ -374,6 +355,47 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 #pragma unroll
             for (int e = 0; e < E; ++e) xv[j][e] = 0.f;
         }
+    }
+    uint32_t xp[TW][DM == 0 ? 1 : E / 2];   // packed 16-bit activation pairs (DM 1, 2)
+    float xoff[TW];                         // DM 1: the offset's share of a chunk's dot product
+    int nsg = 0;                            // DM 1: -sg (+4 for 4-bit codes, which enter as n/16)
+    if constexpr (DM == 1) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < TW; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(xv[j][e]));
+        const int sg = 15 - __builtin_amdgcn_frexp_expf(wave_max(m));
+        nsg = BITS == 8 ? -sg : 4 - sg;
+#pragma unroll
+        for (int j = 0; j < TW; ++j) {
+            _Float16 hv[E];
+            float t = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                hv[e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(xv[j][e], sg));
+                t += static_cast<float>(hv[e]);
+            }
+            xoff[j] = (BITS == 8 ? 1024.f : 1.f) * t;
+            // pair order matches the code pairs built in finish(): 8-bit (4i+2h, 4i+2h+1),
+            // 4-bit (8i+e, 8i+e+4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int h = 0; h < E / 8; ++h) {
+                    const int a = BITS == 8 ? 4 * i + 2 * h : 8 * i + h;
+                    const int b = BITS == 8 ? a + 1 : a + 4;
+                    xp[j][i * (E / 8) + h] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[a])) |
+                                             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[b])) << 16);
+                }
+            }
+        }
+    } else if constexpr (DM == 2) {
+#pragma unroll
+        for (int j = 0; j < TW; ++j)
+#pragma unroll
+            for (int i = 0; i < E / 2; ++i)   // the activations are bf16 values: their fp32 high halves
+                xp[j][i] = (__float_as_uint(xv[j][2 * i]) >> 16) | (__float_as_uint(xv[j][2 * i + 1]) & 0xffff0000u);
     }
 
     auto epilogue = [&](int grp, const float (&t)[NV]) {
@@ -407,39 +429,61 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         __syncthreads();
     };
 
-    auto finish = [&](const u32x4 (&wq)[NV][TW], const f32x2 (&pp)[NL], int grp, int slot) {
+    auto finish = [&](const u32x4 (&wq)[NV][TW], const f32x2 (&pp)[NV][TW], int grp, int slot) {
         if (grp >= n_out) return;   // this stream is past its last group (wave-uniform)
         float tot[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            float acc = 0.f;
+            float acc = 0.f, acc2 = 0.f;
 #pragma unroll
             for (int j = 0; j < TW; ++j) {
                 float dot = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t word = wq[v][j][i];
+                    if constexpr (DM == 1 && BITS == 8) {
+                        const uint32_t c01 = __builtin_amdgcn_perm(0x64646464u, word, 0x04010400u);
+                        const uint32_t c23 = __builtin_amdgcn_perm(0x64646464u, word, 0x04030402u);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c01), __builtin_bit_cast(h16x2, xp[j][2 * i]),
+                                                     dot, false);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c23),
+                                                     __builtin_bit_cast(h16x2, xp[j][2 * i + 1]), dot, false);
+                    } else if constexpr (DM == 1) {
 #pragma unroll
-                    for (int e = 0; e < EPD; ++e) {
-                        float c;
-                        if constexpr (BITS == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
-                        else if constexpr (BITS == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
-                        else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
-                        dot = fmaf(c, xv[j][i * EPD + e], dot);
+                        for (int e = 0; e < 4; ++e) {
+                            // nibbles e and e + 4 into mantissa bits 9..6 of the two halves
+                            const uint32_t sh = e < 2 ? word << (6 - 4 * e) : word >> (4 * e - 6);
+                            const uint32_t ce = (sh & 0x03c003c0u) | 0x3c003c00u;
+                            dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, ce),
+                                                         __builtin_bit_cast(h16x2, xp[j][4 * i + e]), dot, false);
+                        }
+                    } else if constexpr (DM == 2) {
+                        dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, word),
+                                                              __builtin_bit_cast(b16x2, xp[j][i]), dot, false);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPD; ++e) {
+                            float c;
+                            if constexpr (BITS == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
+                            else if constexpr (BITS == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
+                            else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
+                            dot = fmaf(c, xv[j][i * EPD + e], dot);
+                        }
                     }
                 }
                 if constexpr (AFFINE) {
-                    f32x2 pv = pp[0];
-#pragma unroll
-                    for (int i = 1; i < NL; ++i)
-                        if (psel[v][j] == i) pv = pp[i];
-                    const float sc = __int_as_float(__builtin_amdgcn_ds_bpermute(bpa[v][j], __float_as_int(pv.x)));
-                    const float bi = __int_as_float(__builtin_amdgcn_ds_bpermute(bpa[v][j], __float_as_int(pv.y)));
-                    acc += fmaf(sc, dot, bi * xs[j]);
+                    const float sc = pp[v][j].x, bi = pp[v][j].y;
+                    if constexpr (DM == 1) {
+                        acc = fmaf(sc, dot - xoff[j], acc);
+                        acc2 = fmaf(bi, xs[j], acc2);
+                    } else {
+                        acc += fmaf(sc, dot, bi * xs[j]);
+                    }
                 } else {
                     acc += dot;
                 }
             }
+            if constexpr (DM == 1) acc = __builtin_amdgcn_ldexpf(acc, nsg) + acc2;
             tot[v] = wave_total(acc);
         }
         if constexpr (S == 1) {
@@ -475,12 +519,11 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 // times); not for gate/up, whose 16-bit x is shared by the pair's two rows.
 constexpr bool stream_stages_x(bool gu) { return !gu; }
 
-// K split of the streaming kernel for rows of k codes (t 1-KiB K-tiles).
-// Staged activations: two tiles per wave where t splits evenly into at most 8
-// such waves, else one tile per wave for t <= 8.  Activations from global
-// memory: one tile per wave for t <= 8.  Beyond: 8 waves of up to the per-wave
-// register limit.  Returns false when K needs more, or when a staged
-// activation row (xb bytes per element) does not fit in LDS.
+// K split of the streaming kernel for rows of k codes (t 1-KiB K-tiles): two
+// tiles per wave where t splits evenly into at most 8 such waves, one tile
+// per wave for other t <= 8, else 8 waves of up to the per-wave register
+// limit.  Returns false when K needs more, or when a staged activation row
+// (xb bytes per element) does not fit in LDS.
 struct StreamSplit { int s, tw; };
 
 bool stream_split(int bits, int k, int xb, bool stage, StreamSplit& out) {
@@ -488,7 +531,7 @@ bool stream_split(int bits, int k, int xb, bool stage, StreamSplit& out) {
     const int64_t rb = static_cast<int64_t>(k) * bits / 8;
     const int t = static_cast<int>(((rb >> 4) + 63) >> 6);
     const int tw_max = bits == 8 ? 4 : bits == 4 ? 2 : 8;
-    if (stage && t % 2 == 0 && t <= 16) { out = {t / 2, 2}; return true; }
+    if (t % 2 == 0 && t <= 16) { out = {t / 2, 2}; return true; }
     if (t <= 8) { out = {t, 1}; return true; }
     const int tw = (t + 7) / 8;
     if (tw <= tw_max) { out = {8, tw}; return true; }
