@@ -130,14 +130,6 @@ __device__ __forceinline__ float wave_total(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Maximum over the 64 lanes of a wave; every lane gets it (NaNs are ignored
-// unless every lane holds one).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
 // Sum over the 64 lanes of a wave; every lane gets the total.  Fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -193,22 +193,22 @@ qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 // lane for j < TW, and holds the matching fp32 activations (TW*E of them, at
 // most 64) and their sums in registers for the whole launch.
 //
-// For the down projection, whose fp32 activations outweigh the weight bytes
-// that use them (4 bytes per 8-bit code), the row is copied once per block
-// into LDS (each thread moves a few 16-byte pieces) and every wave
+// The activation row is copied once per block into LDS (each thread moves a
+// few 16-byte pieces, issued before the first weight loads) and every wave
 // reads its slice from there: one copy per block instead of one per wave
 // through the vector-memory path, which a CU shares between all of its
-// waves.  For gate/up (16-bit x shared by the pair's two rows) each wave
-// loads its slice directly and a block is a single stream.
+// waves (fp32 h is 4 bytes per 8-bit down code).
 //
-// Each round a wave loads its TW weight chunks of the round's row(s) and
-// the scale/bias pair of each chunk's group (non-temporal: weights are read
-// exactly once) while it reduces the previous round's.  (Loading a wave's
-// pairs once and spreading them with ds_bpermute costs fewer load
-// instructions but puts an LDS round trip on every round's critical path;
-// measured slower.)  Loads are unconditional: a lane past the end of a row or a stream past its last row
-// reads a clamped, valid address and its contribution is zeroed through the
-// activations (0 for such lanes) or not stored.  Row bases are wave-uniform
+// Each round a wave loads its TW weight chunks of the round's row(s) and the
+// scale/bias pair of each chunk's group (non-temporal: weights are read
+// exactly once), reduces them, and only then issues the next round: one
+// round in flight per wave.  Deeper per-wave pipelines (two to six rounds,
+// with the CU's register file spent on them instead of on more waves)
+// measured slower on this part; so did loading a wave's pairs once and
+// spreading them with ds_bpermute (an LDS round trip on every round).  Loads
+// are unconditional: a lane past the end of a row or a stream past its last
+// row reads a clamped, valid address and its contribution is zeroed through
+// the activations (0 for such lanes) or not stored.  Row bases are wave-uniform
 // (scalar registers) and lane offsets 32-bit.  Wave totals come from DPP row
 // reductions; the split-K partials of up to kBatch rounds are parked in LDS
 // and combined in wave order after one barrier per batch, so results are
@@ -233,7 +233,7 @@ constexpr int x_bytes() { return XDT == DT_F32 ? 4 : 2; }
 // Stream (block b, p) takes groups b*P + p + i*G*P for rounds i = 0, 1, ...
 // (G = gridDim); every wave walks the same number of rounds, so the block's
 // barriers line up even when a stream has run out of groups.
-template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P, int NB, bool XL>
+template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P>
 __global__ void __launch_bounds__(64 * S * P)
 qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                     const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
@@ -245,8 +245,6 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     constexpr int NT = 64 * S * P;
     constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
 
-    // XL: activations reach the registers through an LDS copy of the row that
-    // the whole block shares, instead of straight from global memory
     extern __shared__ __align__(16) uint8_t xlds[];   // the activation row, k * x_bytes bytes
     __shared__ float part[(S > 1) ? kBatch : 1][P][S][NV];
 
@@ -268,12 +266,10 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     const u32x4* xg = static_cast<const u32x4*>(xin);
     u32x4* xl = reinterpret_cast<u32x4*>(xlds);
     u32x4 xt[XU];
-    if constexpr (XL) {
 #pragma unroll
-        for (int u = 0; u < XU; ++u) {
-            const int idx = static_cast<int>(threadIdx.x) + u * NT;
-            if (idx < nunits) xt[u] = xg[idx];
-        }
+    for (int u = 0; u < XU; ++u) {
+        const int idx = static_cast<int>(threadIdx.x) + u * NT;
+        if (idx < nunits) xt[u] = xg[idx];
     }
 
     // lane offsets (bytes) of this wave's chunks and of their scale/bias pairs,
@@ -289,8 +285,8 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         soff[j] = AFFINE ? ((cc * E) >> gshift) * 8u : 0u;
     }
 
-    u32x4 wbuf[NB][NV][TW];
-    f32x2 pbuf[NB][NV][TW];
+    u32x4 wbuf[NV][TW];
+    f32x2 pbuf[NV][TW];
 
     // loads of group grp (rows clamped; a stream past its last group reloads row n_out - 1)
     auto issue = [&](u32x4 (&wq)[NV][TW], f32x2 (&pp)[NV][TW], int grp) {
@@ -309,21 +305,17 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         }
     };
 
-    // the first NB - 1 rounds go in flight
-#pragma unroll
-    for (int b = 0; b < NB - 1; ++b)
-        if (g0 + b * GP < n_out) issue(wbuf[b], pbuf[b], g0 + b * GP);
+    // the first round goes in flight before the activations are set up
+    if (g0 < n_out) issue(wbuf, pbuf, g0);
 
     // rest of the activation copy, then this wave's slice
-    if constexpr (XL) {
 #pragma unroll
-        for (int u = 0; u < XU; ++u) {
-            const int idx = static_cast<int>(threadIdx.x) + u * NT;
-            if (idx < nunits) xl[idx] = xt[u];
-        }
-        for (int idx = static_cast<int>(threadIdx.x) + XU * NT; idx < nunits; idx += NT) xl[idx] = xg[idx];
-        __syncthreads();
+    for (int u = 0; u < XU; ++u) {
+        const int idx = static_cast<int>(threadIdx.x) + u * NT;
+        if (idx < nunits) xl[idx] = xt[u];
     }
+    for (int idx = static_cast<int>(threadIdx.x) + XU * NT; idx < nunits; idx += NT) xl[idx] = xg[idx];
+    __syncthreads();
 
     // Dot-product form.  DM 0: fp32 activations, one FMA per code.  DM 1
     // (8/4-bit codes, 16-bit activations): v_dot2_f32_f16 on two codes at a
@@ -332,9 +324,9 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     // byte 0x64 gives 1024 + c (one byte permute per two codes); a 4-bit
     // code n in the top mantissa bits of 1.0 gives 1 + n/16 (a shift and an
     // and-or per two codes), which keeps the offset small against the code.
-    // The activations are held as f16 after a per-wave power-of-two scale
-    // 2^sg that puts the slice maximum in [2^14, 2^15) (a bf16 or f16 value
-    // converts exactly unless it lies more than 2^28 below that maximum); the
+    // The activations are held as f16 after a per-lane power-of-two scale
+    // 2^sg that puts the lane's largest magnitude in [2^14, 2^15) (a bf16 or
+    // f16 value converts exactly unless it lies more than 2^28 below it); the
     // offset's share (1024 or 1 times the chunk's scaled activation sum) is
     // taken off per chunk before the group scale applies, and the powers of
     // two come off once per row.  DM 2 (bf16 weights, bf16 activations):
@@ -347,8 +339,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         xs[j] = 0.f;
         const int c = (ks * TW + j) * 64 + lane;
         if (vj[j]) {
-            if constexpr (XL) load_vec<XDT, E>(xlds, static_cast<int64_t>(c) * E, xv[j]);
-            else load_vec<XDT, E>(xin, static_cast<int64_t>(c) * E, xv[j]);
+            load_vec<XDT, E>(xlds, static_cast<int64_t>(c) * E, xv[j]);
 #pragma unroll
             for (int e = 0; e < E; ++e) xs[j] += xv[j][e];
         } else {
@@ -365,7 +356,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         for (int j = 0; j < TW; ++j)
 #pragma unroll
             for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(xv[j][e]));
-        const int sg = 15 - __builtin_amdgcn_frexp_expf(wave_max(m));
+        const int sg = 15 - __builtin_amdgcn_frexp_expf(m);
         nsg = BITS == 8 ? -sg : 4 - sg;
 #pragma unroll
         for (int j = 0; j < TW; ++j) {
@@ -496,38 +487,27 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         }
     };
 
-    // round i lives in buffer i % NB; round i + NB - 1 is issued before round i is reduced
+    // one round in flight per wave: reduce round i, then issue round i + 1
     int slot = 0, first = 0;
-    for (int i0 = 0; i0 < rounds; i0 += NB) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int i = i0 + b;
-            if (i < rounds) {   // uniform per block
-                const int gi = g0 + (i + NB - 1) * GP;
-                if (gi < n_out) issue(wbuf[(b + NB - 1) % NB], pbuf[(b + NB - 1) % NB], gi);
-                finish(wbuf[b], pbuf[b], g0 + i * GP, slot);
-                if constexpr (S > 1) {
-                    if (++slot == kBatch || i + 1 == rounds) { combine(first, slot); slot = 0; first = i + 1; }
-                }
-            }
+    for (int i = 0; i < rounds; ++i) {   // uniform per block
+        finish(wbuf, pbuf, g0 + i * GP, slot);
+        const int gn = g0 + (i + 1) * GP;
+        if (gn < n_out) issue(wbuf, pbuf, gn);
+        if constexpr (S > 1) {
+            if (++slot == kBatch || i + 1 == rounds) { combine(first, slot); slot = 0; first = i + 1; }
         }
     }
 }
 
-// Whether the streaming kernel stages the activation row in LDS: for the down
-// projection, whose fp32 h outweighs the weight bytes that use it (2 to 8
-// times); not for gate/up, whose 16-bit x is shared by the pair's two rows.
-constexpr bool stream_stages_x(bool gu) { return !gu; }
-
 // K split of the streaming kernel for rows of k codes (t 1-KiB K-tiles): two
 // tiles per wave where t splits evenly into at most 8 such waves, one tile
 // per wave for other t <= 8, else 8 waves of up to the per-wave register
-// limit.  Returns false when K needs more, or when a staged activation row
-// (xb bytes per element) does not fit in LDS.
+// limit.  Returns false when K needs more, or when the activation row (xb
+// bytes per element) does not fit in the LDS stage.
 struct StreamSplit { int s, tw; };
 
-bool stream_split(int bits, int k, int xb, bool stage, StreamSplit& out) {
-    if (stage && static_cast<int64_t>(k) * xb > kStreamLds) return false;
+bool stream_split(int bits, int k, int xb, StreamSplit& out) {
+    if (static_cast<int64_t>(k) * xb > kStreamLds) return false;
     const int64_t rb = static_cast<int64_t>(k) * bits / 8;
     const int t = static_cast<int>(((rb >> 4) + 63) >> 6);
     const int tw_max = bits == 8 ? 4 : bits == 4 ? 2 : 8;
@@ -538,25 +518,18 @@ bool stream_split(int bits, int k, int xb, bool stage, StreamSplit& out) {
     return false;
 }
 
-// Row streams per block: as many as fit in 16 waves while the registers one
-// wave needs (estimated from its double-buffered weight chunks and its slice
-// of activations) stay within what that block size leaves per wave.
-constexpr int stream_rows_per_block(int bits, bool gu, int s, int tw) {
-    const int e = 128 / bits;
-    const int est = (gu ? 2 : 1) * tw * (bits == 16 ? 8 : 12) + tw * (e + 1) + 30;
-    const int waves = est <= 128 ? 16 : est <= 256 ? 8 : 4;
-    return waves / s > 0 ? waves / s : 1;
-}
+// Row streams per block: up to 12 waves, so every wave keeps at least 170
+// VGPRs (three waves per SIMD), more than any split here needs.
+constexpr int stream_rows_per_block(int s) { return s < 12 ? 12 / s : 1; }
 
 template <int BITS, int XDT, int ODT, bool GU, int S, int TW>
 int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s) {
     if constexpr (TW > StreamShape<BITS>::TW_MAX) {
         return static_cast<int>(hipErrorInvalidValue);
     } else {
-        constexpr bool STAGE = stream_stages_x(GU);
-        constexpr int P = STAGE ? stream_rows_per_block(BITS, GU, S, TW) : 1;
-        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, 2, STAGE>;
-        const size_t lds = STAGE ? static_cast<size_t>(k) * x_bytes<XDT>() : 0;
+        constexpr int P = stream_rows_per_block(S);
+        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P>;
+        const size_t lds = static_cast<size_t>(k) * x_bytes<XDT>();
         const int res = resident_blocks(kern, 64 * S * P, lds);
         if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
         const int need = (n_out + P - 1) / P;
@@ -630,7 +603,7 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
     // several rows) the block-per-row-group kernel, rows in blocks of up to 4
     if (m == 1) {
         StreamSplit sp;
-        if (stream_split(w.bits, k, x_bytes<XDT>(), stream_stages_x(GU), sp)) {
+        if (stream_split(w.bits, k, x_bytes<XDT>(), sp)) {
             switch (w.bits) {
                 case 8: return run_stream<8, XDT, ODT, GU>(w, x, r, out, n_out, k, sp, s);
                 case 4: return run_stream<4, XDT, ODT, GU>(w, x, r, out, n_out, k, sp, s);
