@@ -499,11 +499,13 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     }
 }
 
-// K split of the streaming kernel for rows of k codes (t 1-KiB K-tiles): two
-// tiles per wave where t splits evenly into at most 8 such waves, one tile
-// per wave for other t <= 8, else 8 waves of up to the per-wave register
-// limit.  Returns false when K needs more, or when the activation row (xb
-// bytes per element) does not fit in the LDS stage.
+// K split of the streaming kernel for rows of k codes (t 1-KiB K-tiles),
+// from measured sweeps over the Qwen3-8B, Llama-3.2-1B, Llama-3-8B 4-bit and
+// Qwen2.5-1.5B bf16 shapes: one tile per wave for t <= 3 and odd t <= 8, two
+// for other t <= 16, beyond that ceil(t/8) tiles on ceil(t/TW) waves.
+// Returns false when a wave would need more activations than registers
+// allow, or when the activation row (xb bytes per element) does not fit in
+// the LDS stage.
 struct StreamSplit { int s, tw; };
 
 bool stream_split(int bits, int k, int xb, StreamSplit& out) {
@@ -511,23 +513,29 @@ bool stream_split(int bits, int k, int xb, StreamSplit& out) {
     const int64_t rb = static_cast<int64_t>(k) * bits / 8;
     const int t = static_cast<int>(((rb >> 4) + 63) >> 6);
     const int tw_max = bits == 8 ? 4 : bits == 4 ? 2 : 8;
-    if (t % 2 == 0 && t <= 16) { out = {t / 2, 2}; return true; }
-    if (t <= 8) { out = {t, 1}; return true; }
+    if (t <= 3 || (t % 2 == 1 && t <= 8)) { out = {t, 1}; return true; }
+    if (t <= 16) { out = {(t + 1) / 2, 2}; return true; }
     const int tw = (t + 7) / 8;
-    if (tw <= tw_max) { out = {8, tw}; return true; }
-    return false;
+    if (tw > tw_max) return false;
+    out = {(t + tw - 1) / tw, tw};
+    return true;
 }
 
-// Row streams per block: up to 12 waves, so every wave keeps at least 170
-// VGPRs (three waves per SIMD), more than any split here needs.
-constexpr int stream_rows_per_block(int s) { return s < 12 ? 12 / s : 1; }
+// Row streams per block (measured): up to 12 waves per block, and at most 4
+// streams when each wave holds a single tile.  At most 12 waves keeps at
+// least 170 VGPRs per wave (three waves per SIMD), more than any split here
+// needs.
+constexpr int stream_rows_per_block(int s, int tw) {
+    const int p = s < 12 ? 12 / s : 1;
+    return tw == 1 && p > 4 ? 4 : p;
+}
 
 template <int BITS, int XDT, int ODT, bool GU, int S, int TW>
 int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s) {
     if constexpr (TW > StreamShape<BITS>::TW_MAX) {
         return static_cast<int>(hipErrorInvalidValue);
     } else {
-        constexpr int P = stream_rows_per_block(S);
+        constexpr int P = stream_rows_per_block(S, TW);
         auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P>;
         const size_t lds = static_cast<size_t>(k) * x_bytes<XDT>();
         const int res = resident_blocks(kern, 64 * S * P, lds);
@@ -571,8 +579,8 @@ int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int
         case 3: return run_stream_s12<BITS, XDT, ODT, GU, 3>(w, x, r, out, n_out, k, sp.tw, s);
         case 4: return run_stream_s12<BITS, XDT, ODT, GU, 4>(w, x, r, out, n_out, k, sp.tw, s);
         case 5: return run_stream_s12<BITS, XDT, ODT, GU, 5>(w, x, r, out, n_out, k, sp.tw, s);
-        case 6: return run_stream_s12<BITS, XDT, ODT, GU, 6>(w, x, r, out, n_out, k, sp.tw, s);
-        case 7: return run_stream_s12<BITS, XDT, ODT, GU, 7>(w, x, r, out, n_out, k, sp.tw, s);
+        case 6: return run_stream_s<BITS, XDT, ODT, GU, 6>(w, x, r, out, n_out, k, sp.tw, s);
+        case 7: return run_stream_s<BITS, XDT, ODT, GU, 7>(w, x, r, out, n_out, k, sp.tw, s);
         default: return run_stream_s<BITS, XDT, ODT, GU, 8>(w, x, r, out, n_out, k, sp.tw, s);
     }
 }
