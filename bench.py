@@ -14,9 +14,13 @@ dominant kernel's duration comes from HIP events around graph replays of
 that kernel alone.
 
 Prints one JSON line: metric, value (weight-stream GB/s = algorithmic weight
-bytes per layer / time per layer), the time per layer, the fraction of the
-8 TB/s HBM peak, a roofline record for the dominant kernel (gate/up), and the fp64
-CPU oracle timed on a bounded sample on the host cores.
+bytes per layer / time per layer), the time per layer (and its p10/p50/p90
+over single-rotation samples), the fraction of the 8 TB/s HBM peak, a
+roofline record for the dominant kernel (gate/up), the fp64 CPU oracle timed
+on a bounded sample on the host cores, and (unless --no-other-configs) the
+other workloads: Llama-3.2-1B uint8, Qwen2.5-1.5B bf16, Llama-3-8B 4-bit at
+1, 4 and 16 rows (with matrix-core utilisation), add+RMSNorm and a launch
+floor.
 """
 from __future__ import annotations
 
@@ -123,6 +127,91 @@ def kernel_event_times(launch, n_layers, launches):
     return a.elapsed_time(b) / (reps * n_layers) * 1e3
 
 
+def graph_samples(run_step, n_layers, samples):
+    """Per-layer times (us) of `samples` replays of one graph rotation over the
+    n_layers layer sets, each bracketed by HIP events on the launch stream."""
+    import torch
+    for i in range(n_layers):
+        run_step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_layers):
+            run_step(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(samples):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        out.append(a.elapsed_time(b) / n_layers * 1e3)
+    return out
+
+
+def pcts(v):
+    return {"p10": round(float(np.percentile(v, 10)), 3), "p50": round(float(np.percentile(v, 50)), 3),
+            "p90": round(float(np.percentile(v, 90)), 3)}
+
+
+def other_configs(samples):
+    """The other workloads' decode MLP (and the add+RMSNorm row), each over address-distinct
+    weight copies of at least 2 GiB so no weight byte is served from a cache."""
+    import torch
+    import quantized_decode_mlp_amd as qdm
+    res = {}
+    torch_dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+    def dev(a):
+        t = torch.from_numpy(a.raw) if a.dtype == "f32" else \
+            torch.from_numpy(a.raw.view(np.int16)).view(torch_dt[a.dtype])
+        return t.cuda()
+
+    for wi in (2, 3, 5):
+        wl = W.WORKLOADS[wi]
+        g32, u32, d32 = W.weights_f32(wl, 0)
+        if wl.bits == 16:
+            gb, ub, db = (W.to_storage(a, "bf16").raw for a in (g32, u32, d32))
+            q, sb, dq, dsb = qdm.pack_dense_gate_up(gb, ub), None, db, None
+        else:
+            q, sb = qdm.quantize_pack_gate_up(g32, u32, wl.bits, wl.group)
+            dq, dsb = qdm.quantize_pack_rows(d32, wl.bits, wl.group)
+        del g32, u32, d32
+        copies = int(-(-(2 << 30) // wl.weight_bytes))
+        sets = [(qdm.Weight.from_host(wl.ffn, wl.d, wl.bits, wl.group, q, sb),
+                 qdm.Weight.from_host(wl.d, wl.ffn, wl.bits, wl.group, dq, dsb)) for _ in range(copies)]
+        for m in (wl.rows if wi == 5 else (1,)):
+            x, r = W.activations(wl, m)
+            xd, rd = dev(x), dev(r)
+            ws = torch.empty(qdm.mlp_workspace_bytes(m, wl.ffn), dtype=torch.uint8, device="cuda")
+            out = torch.empty_like(rd)
+            t = graph_samples(lambda i: qdm.mlp_decode(xd, rd, *sets[i], workspace=ws, out=out), copies, samples)
+            med = float(np.median(t))
+            rec = {"us_per_layer": pcts(t), "weight_GBps": round(wl.weight_bytes / (med * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(wl.weight_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "copies": copies}
+            if m > 1:
+                flops = 2 * m * 3 * wl.d * wl.ffn
+                rec["mfma_util_bf16"] = round(flops / (med * 1e-6) / 2.5e15, 5)
+            res[f"workload{wi}_m{m}"] = rec
+            _log(f"workload {wi} m={m}: {med:.2f} us/layer")
+        del sets
+        torch.cuda.empty_cache()
+    # add + RMSNorm (the row-a5 kernel) on the Llama-3.2-1B-shaped f16 row, and a launch floor
+    wl = W.WORKLOADS[2]
+    a, b, w = W.rmsnorm_inputs(wl)
+    ad, bd, wd = dev(a), dev(b), dev(w)
+    so, no = torch.empty_like(ad), torch.empty_like(ad)
+    t = graph_samples(lambda i: qdm.add_rmsnorm(ad, bd, wd, wl.norm_eps, s_out=so, n_out=no), 36, samples)
+    res["add_rmsnorm_f16_2048"] = {"us": pcts(t)}
+    z = torch.empty(1, device="cuda")
+    t = graph_samples(lambda i: z.zero_(), 36, samples)
+    res["launch_floor_fill_kernel"] = {"us": pcts(t)}
+    return res
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qwen3_8b_uint8_g128_mlp_hbm_counters.md")
 KERNEL_SOURCES = ["quantized_decode_mlp_amd/csrc/qdm_gemv.hip", "quantized_decode_mlp_amd/csrc/qdm_device.h",
                   "quantized_decode_mlp_amd/csrc/qdm_launch.h"]
@@ -193,6 +282,8 @@ def main(argv=None):
     ap.add_argument("--cpu-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--samples", type=int, default=20, help="graph-rotation samples for percentiles")
+    ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args(argv)
@@ -236,6 +327,7 @@ def main(argv=None):
         t = t_graph
     us = t / args.steps * 1e6
     gbps = wl.weight_bytes / (us * 1e-6) / 1e9
+    spread = pcts(graph_samples(step, n_layers, args.samples))
 
     # dominant kernel (gate/up: 2/3 of the bytes), per-launch events
     gu_bytes = 2 * wl.d * wl.ffn * wl.bits // 8 + 8 * (2 * wl.d * wl.ffn // wl.group)
@@ -262,6 +354,10 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    others = None
+    if not args.no_other_configs:
+        others = other_configs(args.samples)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -292,6 +388,7 @@ def main(argv=None):
             "layer_sets": n_layers, "weight_bytes_per_layer": wl.weight_bytes,
             "launch": "hip graph of 36 layers" if us_graph is not None else "eager",
         },
+        "us_per_layer_samples": spread,
         "eager_us_per_layer": round(us_eager, 3),
         "graph_us_per_layer": None if us_graph is None else round(us_graph, 3),
         "kernels_us": {"gemv_gate_up_swiglu": round(gu_us, 3), "gemv_down_residual": round(dn_us, 3)},
@@ -306,6 +403,7 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": gu_bytes,
         },
         "cpu_baseline": cpu,
+        "other_configs": others,
         "output_finite": finite,
     }
     print(json.dumps(rec), flush=True)
