@@ -139,6 +139,19 @@ def test_rows(m, bits, group):
     _check_mlp(ow, pw, x, r, TOL["bf16"])
 
 
+@pytest.mark.parametrize("m", [2, 7, 16])
+@pytest.mark.parametrize("bits,group", [(8, 64), (8, 32), (4, 32), (16, 0), (4, 128)])
+def test_rows_persistent_gate_up(m, bits, group):
+    """K = 1024 splits evenly over the persistent matrix-core gate/up kernel's
+    waves for every format (its k-block is 32..128 codes); ffn = 896 is 56
+    tiles of 16 (a multiple of every group size)."""
+    d, ffn = 1024, 896
+    ow, pw = generic_case((m, bits, 1), d, ffn, bits, group)
+    x = W.generic_act((m, 6), (m, d), "bf16")
+    r = W.generic_act((m, 7), (m, d), "bf16")
+    _check_mlp(ow, pw, x, r, TOL["bf16"])
+
+
 @pytest.mark.parametrize("m", [3, 16])
 @pytest.mark.parametrize("act", ["f16", "f32"])
 @pytest.mark.parametrize("bits,group", [(8, 32), (4, 64)])
