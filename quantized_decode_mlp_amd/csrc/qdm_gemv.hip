@@ -340,8 +340,10 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         const int c = (ks * TW + j) * 64 + lane;
         if (vj[j]) {
             load_vec<XDT, E>(xlds, static_cast<int64_t>(c) * E, xv[j]);
+            if constexpr (DM != 1) {   // DM 1 takes the sum from the f16 pairs below
 #pragma unroll
-            for (int e = 0; e < E; ++e) xs[j] += xv[j][e];
+                for (int e = 0; e < E; ++e) xs[j] += xv[j][e];
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) xv[j][e] = 0.f;
@@ -361,13 +363,8 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 #pragma unroll
         for (int j = 0; j < TW; ++j) {
             _Float16 hv[E];
-            float t = 0.f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                hv[e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(xv[j][e], sg));
-                t += static_cast<float>(hv[e]);
-            }
-            xoff[j] = (BITS == 8 ? 1024.f : 1.f) * t;
+            for (int e = 0; e < E; ++e) hv[e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(xv[j][e], sg));
             // pair order matches the code pairs built in finish(): 8-bit (4i+2h, 4i+2h+1),
             // 4-bit (8i+e, 8i+e+4)
 #pragma unroll
@@ -380,6 +377,15 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[b])) << 16);
                 }
             }
+            // the chunk's scaled sum (pairs against 1.0), and the unscaled sum for the
+            // bias term: exact scalings of one another
+            float t = 0.f;
+#pragma unroll
+            for (int i = 0; i < E / 2; ++i)
+                t = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, xp[j][i]), __builtin_bit_cast(h16x2, 0x3c003c00u), t,
+                                           false);
+            xoff[j] = (BITS == 8 ? 1024.f : 1.f) * t;
+            xs[j] = __builtin_amdgcn_ldexpf(t, -sg);
         }
     } else if constexpr (DM == 2) {
 #pragma unroll
