@@ -17,6 +17,10 @@ int launch_down_residual(const float* h, const void* r, int m, int act, const qd
 bool mma_rows_supported(const qdm_weight& w, int m);
 int launch_gate_up_mma(const void* x_bf16, int m, const qdm_weight& gu, float* h, void* stream);
 int launch_down_mma(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, void* stream);
+// 2..16 rows, 8/4-bit affine weights, 16-bit activations: persistent blocks
+// streaming the weights once (qdm_mma_stream.hip).
+bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act);
+int launch_gate_up_mma_stream(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream);
 int launch_add_rmsnorm(const void* a, const void* b, const void* w, int rows, int n, float eps,
                        int dtype, void* s_out, void* n_out, void* stream);
 
