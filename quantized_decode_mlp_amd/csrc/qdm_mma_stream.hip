@@ -8,39 +8,34 @@
 // 16-row matrix tile.  Quantization: MLX-LM affine groups, w = scale * q + bias
 // per group of G consecutive k of a row.
 //
-// Matrix-core form: v_mfma_f32_16x16x32_f16 computes D[16 m][16 n] +=
+// Matrix-core form: v_mfma_f32_16x16x32_{bf16,f16} computes D[16 m][16 n] +=
 // A[16 m][32 k] * B[32 k][16 n].  Lane l supplies A row m = l % 16 and B column
 // n = l % 16 for the eight k of slot kq = l / 16, and holds D rows
 // 4 kq + 0..3 of column l % 16.  A is the activation rows (rows at or past the
 // caller's m are zero), B a tile of 16 weight rows.
 //
-// Exact operands.  A code enters B as an exact f16 value by placing its bits
-// in the mantissa under a fixed exponent: an 8-bit code c gives 1024 + c (one
-// byte permute per two codes), a 4-bit code c gives 1 + c/16 (a shift and an
-// and-or per two codes; the small offset keeps the fp32 accumulation far from
-// cancellation).  The activations are staged once per block in LDS as f16
-// after a per-row power-of-two scale that puts the row's largest magnitude in
-// [2^14, 2^15): bf16 and f16 values convert exactly unless they lie more than
-// 2^28 below that maximum.  For each fold chunk of k (one quantization group,
-// or 64 k when the group is wider) the partial tile P = sum (off + mul c) x'
-// is folded in fp32 as
-//     acc += (scale / mul) * (P - off * X') + bias * X',
-// X' the chunk's sum of the staged activations (kept in LDS), so no weight is
-// dequantized before the MMA.  The row scale comes off in the epilogue.
+// Exact operands.  The MMA runs in the activations' own 16-bit type, so the
+// activations are staged once per block in LDS as they are, with the fp32 sum
+// X of every fold chunk (one quantization group, or the k-block when the
+// group is wider).  A code enters B as an exact value off + c/inv (see
+// StepCodes), and the chunk's partial tile P = sum (off + c/inv) x is folded
+// in fp32 as
+//     acc += scale * inv * P + (bias - scale * inv * off) * X,
+// which is scale * sum c x + bias * X: no weight is dequantized before the MMA.
 //
-// Lane k assignment inside a 64-wide k-block: with groups of 64 or more, lane
-// kq holds k 16 kq + 8 t + e for k-steps t = 0, 1 (one 8- or 16-byte load per
-// row); with 32-wide groups it holds k 32 t + 8 kq + e (one load per step), so
-// that every k-step lies in one group.
+// Lane k assignment: see BlockLayout (16-byte code loads per lane and row
+// whenever the quantization group allows it).
 //
 // Work split: a block is S x P waves.  Wave (ks, p) takes 16-row tiles
-// b*P + p + i*G*P (G = grid size) and, of each tile, the 64-wide k-blocks
-// ks, ks + S, ks + 2S, ...; the next U k-blocks (crossing into the next tile)
-// are always in flight.  The S partial tiles meet in LDS and are summed in
-// wave order.  In the packed gate/up layout rows 2n and 2n + 1 are gate and up
+// b*P + p + i*G*P (G = grid size) and, of each tile, the ks-th contiguous
+// 1/S of its k-blocks, with the next U k-blocks (crossing into the next tile)
+// in flight and the tile's scale/bias pairs for that range loaded once.  The
+// S partial tiles meet in LDS and are summed in wave order.  In the packed gate/up layout rows 2n and 2n + 1 are gate and up
 // of output n, so one tile reads 32 packed rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "qdm_device.h"
 #include "qdm_internal.h"
@@ -51,6 +46,7 @@ namespace {
 
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -60,27 +56,54 @@ constexpr int kRows = 16;     // rows of the matrix tile
 constexpr int kPad = 8;       // f16 padding per staged row: 16 bytes, four LDS banks per row
 constexpr int kLdsCap = 160 * 1024;
 
-__device__ __forceinline__ f32x4 mma_f16(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, a), __builtin_bit_cast(h16x8, b), c, 0,
-                                                  0, 0);
+// 16x16x32 MMA in the activations' 16-bit type (bf16 or f16 operands)
+template <int XDT>
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (XDT == DT_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, a), __builtin_bit_cast(h16x8, b), c, 0,
+                                                      0, 0);
 }
 
-// The eight codes of one lane and k-step as f16 operand values off + mul * c.
-template <int BITS>
+// The eight codes of one lane and k-step as exact operand values off + c / inv
+// in the MMA's 16-bit type.  8-bit codes: f16 1024 + c (the byte under the
+// exponent byte 0x64, one permute per two codes) or the bf16 integer c (an
+// exact byte conversion and a permute of the high halves; no offset).  4-bit
+// codes: 1 + c/16 in either type (the nibble in the top mantissa bits of 1.0,
+// a shift and an and-or per two codes); element pairs (e, e + 4), so the
+// staged activations take that order too.
+template <int BITS, int XDT>
 struct StepCodes;
 
+template <int BITS>
+struct StepWords;
+
 template <>
-struct StepCodes<8> {
-    using raw = u32x2;     // codes k + 0..7, one byte each
-    using words = u32x4;   // two k-steps
-    __device__ __forceinline__ static raw step(const words& w, int t) { return u32x2{w[2 * t], w[2 * t + 1]}; }
-    __device__ __forceinline__ static void set_step(words& w, int t, raw r) {
+struct StepWords<8> {
+    using raw = u32x2;   // codes k + 0..7, one byte each
+    template <class W>
+    __device__ __forceinline__ static raw step(const W& w, int t) { return u32x2{w[2 * t], w[2 * t + 1]}; }
+    template <class W>
+    __device__ __forceinline__ static void set_step(W& w, int t, raw r) {
         w[2 * t] = r[0];
         w[2 * t + 1] = r[1];
     }
-    static constexpr float kOff = 1024.f;
-    static constexpr float kInvMul = 1.f;
-    // element e of the operand holds the code of k + e
+};
+
+template <>
+struct StepWords<4> {
+    using raw = uint32_t;   // codes k + 0..7, low nibble first
+    template <class W>
+    __device__ __forceinline__ static raw step(const W& w, int t) { return w[t]; }
+    template <class W>
+    __device__ __forceinline__ static void set_step(W& w, int t, raw r) { w[t] = r; }
+};
+
+template <>
+struct StepCodes<8, DT_F16> : StepWords<8> {
+    static constexpr float kOff = 1024.f, kInvMul = 1.f;
     __device__ __forceinline__ static u32x4 operand(raw w) {
         return u32x4{__builtin_amdgcn_perm(0x64646464u, w[0], 0x04010400u),
                      __builtin_amdgcn_perm(0x64646464u, w[0], 0x04030402u),
@@ -90,52 +113,77 @@ struct StepCodes<8> {
 };
 
 template <>
-struct StepCodes<4> {
-    using raw = uint32_t;   // codes k + 0..7, low nibble first
-    using words = u32x2;    // two k-steps
-    __device__ __forceinline__ static raw step(const words& w, int t) { return w[t]; }
-    __device__ __forceinline__ static void set_step(words& w, int t, raw r) { w[t] = r; }
-    static constexpr float kOff = 1.f;
-    static constexpr float kInvMul = 16.f;
-    // nibbles e and e + 4 into mantissa bits 9..6 of the two halves of 1.0:
-    // operand elements 2e and 2e + 1 hold the codes of k + e and k + e + 4
+struct StepCodes<8, DT_BF16> : StepWords<8> {
+    static constexpr float kOff = 0.f, kInvMul = 1.f;
+    // element 0 (low half) = a, element 1 = b, both exact bf16 values
+    __device__ __forceinline__ static uint32_t pack_hi(float a, float b) {
+        return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+    }
+    __device__ __forceinline__ static u32x4 operand(raw w) {
+        auto byte = [](uint32_t v, int i) { return static_cast<float>((v >> (8 * i)) & 0xffu); };
+        return u32x4{pack_hi(byte(w[0], 0), byte(w[0], 1)), pack_hi(byte(w[0], 2), byte(w[0], 3)),
+                     pack_hi(byte(w[1], 0), byte(w[1], 1)), pack_hi(byte(w[1], 2), byte(w[1], 3))};
+    }
+};
+
+template <>
+struct StepCodes<4, DT_F16> : StepWords<4> {
+    static constexpr float kOff = 1.f, kInvMul = 16.f;
+    // mantissa bits 9..6 of f16 1.0
     __device__ __forceinline__ static u32x4 operand(raw w) {
         return u32x4{((w << 6) & 0x03c003c0u) | 0x3c003c00u, ((w << 2) & 0x03c003c0u) | 0x3c003c00u,
                      ((w >> 2) & 0x03c003c0u) | 0x3c003c00u, ((w >> 6) & 0x03c003c0u) | 0x3c003c00u};
     }
 };
 
-// Position, inside an aligned group of eight staged activations, of the
-// activation of k offset e: the order the codes take in the operand.
-template <int BITS>
-__device__ __forceinline__ int slot_of(int e) {
-    return BITS == 4 ? ((e & 3) << 1) | (e >> 2) : e;
-}
+template <>
+struct StepCodes<4, DT_BF16> : StepWords<4> {
+    static constexpr float kOff = 1.f, kInvMul = 16.f;
+    // mantissa bits 6..3 of bf16 1.0
+    __device__ __forceinline__ static u32x4 operand(raw w) {
+        return u32x4{((w << 3) & 0x00780078u) | 0x3f803f80u, ((w >> 1) & 0x00780078u) | 0x3f803f80u,
+                     ((w >> 5) & 0x00780078u) | 0x3f803f80u, ((w >> 9) & 0x00780078u) | 0x3f803f80u};
+    }
+};
+
+// k-block layout.  WIDE (groups of 64 or more): a k-block is KBK k, lane kq
+// holds the LK = KBK/4 consecutive k from LK*kq (one 16-byte load per row),
+// k-step t takes its codes 8t .. 8t+7; a block spanning NF > 1 groups runs
+// each step once per group with the activation kept only on that group's
+// lanes.  Otherwise (32-wide groups) a k-block is 64 k, lane kq holds k
+// 32t + 8kq .. +7 of step t (one load per step) and each step is one group.
+template <int BITS, int G>
+struct BlockLayout {
+    static constexpr bool WIDE = G >= 64;
+    static constexpr int KBK = (BITS == 4 && WIDE) ? 128 : 64;
+    static constexpr int STEPS = KBK / 32;
+    static constexpr int LK = KBK / 4;
+    static constexpr int FG = WIDE ? (G < KBK ? G : KBK) : 32;   // fold chunk (k)
+    static constexpr int NF = KBK / FG;                           // fold chunks per k-block
+    using Words = typename std::conditional<WIDE || BITS == 8, u32x4, u32x2>::type;
+};
 
 __host__ __device__ constexpr size_t round16(size_t v) { return (v + 15) & ~static_cast<size_t>(15); }
 
-template <int G>
-constexpr int fold_width() { return G < 64 ? G : 64; }
-
 // Dynamic LDS of the gate/up kernel: staged rows, then the fold-chunk sums.
-template <int G>
+template <int BITS, int G>
 size_t gate_up_lds_bytes(int m, int k) {
-    return round16(static_cast<size_t>(m) * (k + kPad) * 2) + static_cast<size_t>(k / fold_width<G>()) * kRows * 4;
+    return round16(static_cast<size_t>(m) * (k + kPad) * 2) +
+           static_cast<size_t>(k / BlockLayout<BITS, G>::FG) * kRows * 4;
 }
 
 template <int BITS, int XDT, int G, int S, int P, int U, int XPT, int NPL>
 __global__ void __launch_bounds__(64 * S * P)
 qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, const void* __restrict__ xin,
                           float* __restrict__ hout, int N, int K, int m_rows) {
-    using SC = StepCodes<BITS>;
+    using SC = StepCodes<BITS, XDT>;
+    using L = BlockLayout<BITS, G>;
     constexpr int NT = 64 * S * P;
-    constexpr int FG = fold_width<G>();   // fold chunk (k)
-    constexpr int FPB = 64 / FG;          // fold chunks per k-block: 1 or 2
-    constexpr int SPF = FG / 32;          // k-steps per fold chunk: 1 or 2
+    constexpr int KBK = L::KBK, STEPS = L::STEPS, NF = L::NF, FG = L::FG;
+    constexpr bool WIDE = L::WIDE;
+    constexpr int CPF = FG / 8;   // 16-byte activation pieces per fold chunk
 
     extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ float rowmax[kRows];
-    __shared__ float unscale[kRows];
     __shared__ f32x4 part[S > 1 ? S - 1 : 1][P][2][64];
 
     const int lane = threadIdx.x & 63;
@@ -147,8 +195,8 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
     float* xsum = reinterpret_cast<float*>(lds + round16(static_cast<size_t>(m_rows) * ldx * 2));
 
     const int ntiles = N / kRows;
-    const int nkw = K / 64 / S;              // this wave's k-blocks per tile: kb = ks * nkw + j
-    const int gw = nkw * 64 / G;             // and their groups: gbase + 0 .. gw - 1
+    const int nkw = K / KBK / S;             // this wave's k-blocks per tile: kb = ks * nkw + j
+    const int gw = nkw * KBK / G;            // and their groups: gbase + 0 .. gw - 1
     const int gbase = ks * gw;
     const int GP = static_cast<int>(gridDim.x) * P;
     const int t0 = static_cast<int>(blockIdx.x) * P + p;
@@ -168,21 +216,16 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         if (u < npieces) xt[j] = xg[u];
     }
 
-    // the lane's 16 codes of a k-block (two k-steps): one load when a k-block
-    // lies inside one group (lane kq holds k 16 kq + 8 t + e), else one load
-    // per k-step (lane kq holds k 32 t + 8 kq + e) so that each step stays in
-    // its own 32-wide group
-    constexpr bool WIDE = G >= 64;
-    using Words = typename SC::words;
+    using Words = typename L::Words;
     struct Stage {
-        Words c[2];   // [gate, up]
+        Words c[2];   // [gate, up]: the lane's codes of one k-block
     };
     Stage st[U];
     const int nflat = rounds * nkw;
 
     // Scale/bias pairs of the wave's groups for one tile, 16 bytes a lane:
     // register r of lane (row li, slot kq) holds groups gbase + 8r + 2kq, +1;
-    // a k-block takes its pair from lane li + 16 * slot with a shuffle.
+    // a fold chunk takes its pair from lane li + 16 * slot with a shuffle.
     f32x4 pw[2][NPL];
     auto load_pairs = [&](int i) {
         const int tile = t0 + i * GP;
@@ -218,12 +261,12 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
             const uint32_t row = 2u * static_cast<uint32_t>(tile * kRows + li) + v;
             const uint8_t* qrow = q + static_cast<size_t>(row) * rb;
             if constexpr (WIDE) {
-                const uint32_t k0 = static_cast<uint32_t>(kb * 64 + 16 * kq);
+                const uint32_t k0 = static_cast<uint32_t>(kb * KBK + L::LK * kq);
                 s.c[v] = *reinterpret_cast<const Words*>(qrow + k0 * BITS / 8);
             } else {
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint32_t k0 = static_cast<uint32_t>(kb * 64 + 32 * t + 8 * kq);
+                for (int t = 0; t < STEPS; ++t) {
+                    const uint32_t k0 = static_cast<uint32_t>(kb * KBK + 32 * t + 8 * kq);
                     SC::set_step(s.c[v], t, *reinterpret_cast<const typename SC::raw*>(qrow + k0 * BITS / 8));
                 }
             }
@@ -235,76 +278,48 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
     for (int u = 0; u < U; ++u)
         if (u < nflat) issue(st[u], u);
 
-    // stage the rows: raw 16-bit values into the padded rows
-    for (int j = 0; j < XPT; ++j) {
-        const int u = static_cast<int>(threadIdx.x) + j * NT;
-        if (u < npieces) {
-            const int m = u / ppr, c = u - m * ppr;
-            *reinterpret_cast<u32x4*>(xs + m * ldx + c * 8) = xt[j];
-        }
-    }
-    for (int u = static_cast<int>(threadIdx.x) + XPT * NT; u < npieces; u += NT) {
-        const int m = u / ppr, c = u - m * ppr;
-        *reinterpret_cast<u32x4*>(xs + m * ldx + c * 8) = xg[u];
-    }
-    __syncthreads();
-
-    auto to_f32 = [](uint32_t bits16) -> float {
-        if constexpr (XDT == DT_BF16) return __uint_as_float(bits16 << 16);
-        else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
-    };
-    // per-row largest magnitude: wave w takes rows w, w + S*P, ...
-    for (int m = w; m < m_rows; m += S * P) {
-        float mx = 0.f;
-        for (int c = lane; c < ppr; c += 64) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(xs + m * ldx + c * 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                mx = fmaxf(mx, fmaxf(fabsf(to_f32(v[e] & 0xffffu)), fabsf(to_f32(v[e] >> 16))));
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (lane == 0) rowmax[m] = mx;
-    }
-    __syncthreads();
-
-    // scaled f16 in place (operand order), and the fold-chunk sums X' (zero for rows past m)
-    const int nchunks = K / FG;
-    for (int u = static_cast<int>(threadIdx.x); u < nchunks * kRows; u += NT) {
-        const int m = u % kRows, ch = u / kRows;
+    // Stage the rows in LDS as they are (operand order for 4-bit codes) with
+    // the fp32 sum of each fold chunk: a piece's sum, then the sum over the
+    // chunk's CPF consecutive lanes.  Sums of rows past m are zero.
+    auto stage_piece = [&](int u, const u32x4& v) {
         float sum = 0.f;
-        if (m < m_rows) {
-            const int sg = 15 - __builtin_amdgcn_frexp_expf(rowmax[m]);
-#pragma unroll
-            for (int c8 = 0; c8 < FG / 8; ++c8) {
-                uint16_t* piece = xs + m * ldx + ch * FG + c8 * 8;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(piece);
-                uint16_t o[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t b16 = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
-                    const _Float16 hv = static_cast<_Float16>(__builtin_amdgcn_ldexpf(to_f32(b16), sg));
-                    o[slot_of<BITS>(e)] = __builtin_bit_cast(uint16_t, hv);
-                }
-                // the words are built in a plain array: assigning the lanes of a
-                // vector one by one and feeding each to v_dot2 as it is built
-                // compiled to dot products that all read the first word
-                uint32_t rw[4];
+        int m = 0, c = 0;
+        if (u < npieces) {
+            m = u / ppr;
+            c = u - m * ppr;
+            u32x4 o = v;
+            if constexpr (BITS == 4) {
+                // elements (0, 4), (1, 5), (2, 6), (3, 7) of the piece per word
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    rw[i] = static_cast<uint32_t>(o[2 * i]) | (static_cast<uint32_t>(o[2 * i + 1]) << 16);
+                    o[i] = __builtin_amdgcn_perm(v[2 + (i >> 1)], v[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
+            }
+            *reinterpret_cast<u32x4*>(xs + m * ldx + c * 8) = o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, rw[i]), __builtin_bit_cast(h16x2, 0x3c003c00u),
+            for (int i = 0; i < 4; ++i) {
+                // the word goes through a scalar: __builtin_bit_cast of a vector
+                // element expression reinterprets the vector's first element
+                const uint32_t word = v[i];
+                if constexpr (XDT == DT_BF16)
+                    sum += __uint_as_float(word << 16) + __uint_as_float(word & 0xffff0000u);
+                else
+                    sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), __builtin_bit_cast(h16x2, 0x3c003c00u),
                                                  sum, false);
-                *reinterpret_cast<u32x4*>(piece) = u32x4{rw[0], rw[1], rw[2], rw[3]};
             }
         }
-        xsum[ch * kRows + m] = sum;
+#pragma unroll
+        for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
+        if (u < npieces && c % CPF == 0) xsum[(c / CPF) * kRows + m] = sum;
+    };
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) stage_piece(static_cast<int>(threadIdx.x) + j * NT, xt[j]);
+    for (int u0 = XPT * NT; u0 < npieces; u0 += NT) {
+        const int u = u0 + static_cast<int>(threadIdx.x);
+        stage_piece(u, u < npieces ? xg[u] : u32x4{0u, 0u, 0u, 0u});
     }
-    if (threadIdx.x < kRows) {
-        const int m = static_cast<int>(threadIdx.x);
-        unscale[m] = m < m_rows ? __builtin_amdgcn_ldexpf(1.f, __builtin_amdgcn_frexp_expf(rowmax[m]) - 15) : 0.f;
+    for (int u = static_cast<int>(threadIdx.x); u < (K / FG) * (kRows - m_rows); u += NT) {
+        const int ch = u / (kRows - m_rows), m = m_rows + (u - ch * (kRows - m_rows));
+        xsum[ch * kRows + m] = 0.f;
     }
     __syncthreads();
 
@@ -316,26 +331,40 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         if (t0 + i * GP >= ntiles) return;   // wave-uniform
         if (j == 0 && i > 0) load_pairs(i);
         const int kb = ks * nkw + j;
+        // one partial tile per fold chunk; a wide k-block spanning NF groups runs
+        // every step once per chunk with the activation kept only on the lanes
+        // whose k lie in that chunk, a narrow one gives step t to chunk t
+        f32x4 pt[NF][2];
 #pragma unroll
-        for (int fi = 0; fi < FPB; ++fi) {
-            f32x4 pt[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int fc = 0; fc < NF; ++fc) pt[fc][0] = pt[fc][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ts = 0; ts < SPF; ++ts) {
-                const int t = fi * SPF + ts;
-                u32x4 a = u32x4{0u, 0u, 0u, 0u};
-                const int ka = WIDE ? kb * 64 + 16 * kq + 8 * t : kb * 64 + 32 * t + 8 * kq;
-                if (arow) a = *reinterpret_cast<const u32x4*>(xs + li * ldx + ka);
-                pt[0] = mma_f16(a, SC::operand(SC::step(s.c[0], t)), pt[0]);
-                pt[1] = mma_f16(a, SC::operand(SC::step(s.c[1], t)), pt[1]);
+        for (int t = 0; t < STEPS; ++t) {
+            const int ka = WIDE ? kb * KBK + L::LK * kq + 8 * t : kb * KBK + 32 * t + 8 * kq;
+            const u32x4 a = arow ? *reinterpret_cast<const u32x4*>(xs + li * ldx + ka) : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 bg = SC::operand(SC::step(s.c[0], t)), bu = SC::operand(SC::step(s.c[1], t));
+#pragma unroll
+            for (int fc = 0; fc < NF; ++fc) {
+                if constexpr (!WIDE) {
+                    if (t != fc) continue;
+                }
+                u32x4 at = a;
+                if constexpr (WIDE && NF > 1) {
+                    if ((kq * L::LK) / FG != fc) at = u32x4{0u, 0u, 0u, 0u};
+                }
+                pt[fc][0] = mma<XDT>(at, bg, pt[fc][0]);
+                pt[fc][1] = mma<XDT>(at, bu, pt[fc][1]);
             }
-            const f32x4 xc = *reinterpret_cast<const f32x4*>(xsum + ((kb * 64) / FG + fi) * kRows + 4 * kq);
+        }
+#pragma unroll
+        for (int fc = 0; fc < NF; ++fc) {
+            const f32x4 xc = *reinterpret_cast<const f32x4*>(xsum + ((kb * KBK) / FG + fc) * kRows + 4 * kq);
 #pragma unroll
             for (int v = 0; v < 2; ++v) {
-                const f32x2 pv = pair_of(v, (j * 64 + fi * FG) / G);
-                const float se = pv.x * SC::kInvMul, bi = pv.y;
+                const f32x2 pv = pair_of(v, (j * KBK + fc * FG) / G);
+                // scale * sum c x + bias * X with sum c x = inv * (P - off * X)
+                const float se = pv.x * SC::kInvMul, be = fmaf(-SC::kOff, se, pv.y);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[v][e] = fmaf(se, fmaf(-SC::kOff, xc[e], pt[v][e]), fmaf(bi, xc[e], acc[v][e]));
+                for (int e = 0; e < 4; ++e) acc[v][e] = fmaf(se, pt[fc][v][e], fmaf(be, xc[e], acc[v][e]));
             }
         }
     };
@@ -363,7 +392,7 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
             for (int e = 0; e < 4; ++e) {
                 const int m = 4 * kq + e;
                 if (m < m_rows) {
-                    const float g = acc[0][e] * unscale[m], uu = acc[1][e] * unscale[m];
+                    const float g = acc[0][e], uu = acc[1][e];
                     hout[static_cast<int64_t>(m) * N + tile * kRows + li] = g / (1.0f + expf(-g)) * uu;
                 }
             }
@@ -398,9 +427,11 @@ constexpr int pair_regs() { return G == 32 ? 4 : 2; }
 template <int BITS, int XDT, int G>
 int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s) {
     constexpr int NT = 64 * kS * kP;
-    constexpr int XPT = 8;
-    auto kern = qmm_gate_up_stream_kernel<BITS, XDT, G, kS, kP, kU, XPT, pair_regs<G>()>;
-    const size_t lds = gate_up_lds_bytes<G>(m, w.k);
+    constexpr int XPT = 4;
+    // the same bytes in flight per wave: four 64-wide or two 128-wide k-blocks
+    constexpr int U = BlockLayout<BITS, G>::KBK == 128 ? kU / 2 : kU;
+    auto kern = qmm_gate_up_stream_kernel<BITS, XDT, G, kS, kP, U, XPT, pair_regs<G>()>;
+    const size_t lds = gate_up_lds_bytes<BITS, G>(m, w.k);
     const int res = resident_blocks(kern, NT, lds);
     if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
     const int ntiles = w.n / kRows;
@@ -431,14 +462,19 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
     if (w.bits != 8 && w.bits != 4) return false;
     if (w.group != 32 && w.group != 64 && w.group != 128) return false;
     if (act != DT_BF16 && act != DT_F16) return false;
-    if (w.n % kRows != 0 || w.k % (64 * kS) != 0) return false;
+    const int kbk = (w.bits == 4 && w.group >= 64) ? 128 : 64;
+    if (w.n % kRows != 0 || w.k % (kbk * kS) != 0) return false;
     // each wave's groups: a whole, even number, at most 8 per pair register
     const int gw = w.k / kS / w.group;
     const int npl = w.group == 32 ? pair_regs<32>() : pair_regs<64>();
     if (gw * w.group * kS != w.k || gw % 2 != 0 || gw > 8 * npl) return false;
     // staged rows, chunk sums and the combine buffer within one CU's LDS
-    const size_t lds = (w.group == 32 ? gate_up_lds_bytes<32>(m, w.k) : gate_up_lds_bytes<64>(m, w.k)) +
-                       static_cast<size_t>(kS - 1) * kP * 2 * 64 * 16 + 2 * kRows * 4;
+    const size_t dyn = w.bits == 4 ? (w.group == 32 ? gate_up_lds_bytes<4, 32>(m, w.k)
+                                      : w.group == 64 ? gate_up_lds_bytes<4, 64>(m, w.k)
+                                                      : gate_up_lds_bytes<4, 128>(m, w.k))
+                                   : (w.group == 32 ? gate_up_lds_bytes<8, 32>(m, w.k)
+                                                    : gate_up_lds_bytes<8, 64>(m, w.k));
+    const size_t lds = dyn + static_cast<size_t>(kS - 1) * kP * 2 * 64 * 16 + 2 * kRows * 4;
     return lds <= kLdsCap;
 }
 
