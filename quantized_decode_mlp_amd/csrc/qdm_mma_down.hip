@@ -1,0 +1,395 @@
+// Few-row (2..16 rows) down projection with the residual, 8/4-bit affine
+// weights, on the gfx950 matrix cores: y = r + W_down h for fp32 h [m][K].
+//
+// Pages: meTile docs, "MLX-LM Backend", section "Dispatch Policy" (several
+// activation rows go to 16-row matrix tiles, ragged row counts masked in the
+// tile); "Compute-Graph Fusion" for the residual fused into the projection.
+// Quantization: MLX-LM affine groups, w = scale * q + bias.
+//
+// The hidden row is long (K = ffn) and fp32, so no block can stage all of it:
+// K is split into NS slices.  Kernel 1: block (slice s, tile group) stages
+// h[:, slice] in LDS as a bf16 high part and the bf16 remainder
+// (h = hi + lo to about 16 significant bits) with the fp32 sum X of every
+// fold chunk, then streams 16-row weight tiles of that slice through
+// v_mfma_f32_16x16x32_bf16 (two MMAs per k-step, hi and lo) with the codes as
+// exact operands and each chunk's partial folded as in the gate/up kernel;
+// the partial tile goes to part[s][m][n].  Kernel 2 adds the NS partials in
+// slice order and the residual and rounds to the output type.  Work split,
+// lane layout and scale/bias handling match the gate/up kernel: S waves take
+// contiguous quarters of a tile's k-range in the slice, P tiles per block,
+// tiles t0 + i * GP over rounds i.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "qdm_device.h"
+#include "qdm_internal.h"
+#include "qdm_launch.h"
+#include "qdm_mma_common.h"
+
+namespace qdm {
+namespace {
+
+// One wave per tile over the block's whole slice (no cross-wave combine), 16
+// tiles per block, k-blocks in flight as in gate/up.
+constexpr int kDS = 1, kDP = 16, kDU = 4;
+
+// Dynamic LDS of the down kernel: hi rows, lo rows, fold-chunk sums.
+template <int BITS, int G>
+size_t down_lds_bytes(int m, int kr) {
+    return 2 * round16(static_cast<size_t>(m) * (kr + kPad) * 2) +
+           static_cast<size_t>(kr / BlockLayout<BITS, G>::FG) * kRows * 4;
+}
+
+template <int BITS, int G, int S, int P, int U, int NPL>
+__global__ void __launch_bounds__(64 * S * P)
+qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, const float* __restrict__ h,
+                     float* __restrict__ part, int N, int K, int KR, int TB, int m_rows) {
+    using SC = StepCodes<BITS, DT_BF16>;
+    using L = BlockLayout<BITS, G>;
+    constexpr int KBK = L::KBK, STEPS = L::STEPS, NF = L::NF, FG = L::FG;
+    constexpr bool WIDE = L::WIDE;
+    constexpr int CPF = FG / 8;   // 8-value pieces per fold chunk
+
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ f32x4 comb[S > 1 ? S - 1 : 1][P][64];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = w % S, p = w / S;
+    const int li = lane & 15, kq = lane >> 4;
+    const int NS = K / KR;
+    const int ksl = static_cast<int>(blockIdx.x) % NS, tb = static_cast<int>(blockIdx.x) / NS;
+    const int ldx = KR + kPad;
+    const size_t rows_bytes = round16(static_cast<size_t>(m_rows) * ldx * 2);
+    uint16_t* xh = reinterpret_cast<uint16_t*>(lds);
+    uint16_t* xl = reinterpret_cast<uint16_t*>(lds + rows_bytes);
+    float* xsum = reinterpret_cast<float*>(lds + 2 * rows_bytes);
+
+    const int ntiles = N / kRows;
+    const int kw = KR / S;                   // this wave's k-range of the slice
+    const int nkw = kw / KBK;
+    const int k0w = ksl * KR + ks * kw;      // its first k in the row
+    const int gw = kw / G;
+    const int gbase = k0w / G;
+    const int GP = TB * P;
+    const int t0 = tb * P + p;
+    const int rounds = (ntiles - tb * P + GP - 1) / GP;   // same for the block
+    if (rounds <= 0) return;   // uniform per block, before any barrier
+    const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;
+    const int ngroups = K / G;
+
+    using Words = typename L::Words;
+    Words st[U];
+    const int nflat = rounds * nkw;
+
+    f32x4 pw[NPL];
+    auto load_pairs = [&](int i) {
+        const int tile = t0 + i * GP;
+        if (tile >= ntiles) return;   // wave-uniform
+        const size_t row = static_cast<uint32_t>(tile * kRows + li);
+#pragma unroll
+        for (int r = 0; r < NPL; ++r) {
+            const int g = 8 * r + 2 * kq;
+            if (g < gw) pw[r] = *reinterpret_cast<const f32x4*>(sb + 2 * (row * ngroups + gbase + g));
+        }
+    };
+    auto pair_of = [&](int gl) -> f32x2 {
+        const int r = gl >> 3, src = li + 16 * ((gl & 7) >> 1);
+        f32x4 q4 = pw[0];
+#pragma unroll
+        for (int rr = 1; rr < NPL; ++rr)
+            if (r == rr) q4 = pw[rr];
+        const float x = (gl & 1) ? q4[2] : q4[0], y = (gl & 1) ? q4[3] : q4[1];
+        return f32x2{__shfl(x, src, 64), __shfl(y, src, 64)};
+    };
+    auto issue = [&](Words& c, int f) {
+        const int i = f / nkw, j = f - i * nkw;
+        const int tile = t0 + i * GP;
+        if (tile >= ntiles) return;   // wave-uniform
+        const uint8_t* qrow = q + static_cast<size_t>(tile * kRows + li) * rb;
+        const int kb0 = k0w + j * KBK;
+        if constexpr (WIDE) {
+            c = *reinterpret_cast<const Words*>(qrow + static_cast<uint32_t>(kb0 + L::LK * kq) * BITS / 8);
+        } else {
+#pragma unroll
+            for (int t = 0; t < STEPS; ++t)
+                SC::set_step(c, t,
+                             *reinterpret_cast<const typename SC::raw*>(
+                                 qrow + static_cast<uint32_t>(kb0 + 32 * t + 8 * kq) * BITS / 8));
+        }
+    };
+
+    load_pairs(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (u < nflat) issue(st[u], u);
+
+    // stage h[:, slice] as bf16 hi + lo (operand order for 4-bit codes) and the
+    // fold-chunk sums of hi + lo; sums of rows past m are zero
+    const int ppr = KR / 8;
+    const int npieces = m_rows * ppr;
+    auto pack2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
+    for (int u0 = 0; u0 < npieces; u0 += 64 * S * P) {
+        const int u = u0 + static_cast<int>(threadIdx.x);
+        float sum = 0.f;
+        int m = 0, c = 0;
+        if (u < npieces) {
+            m = u / ppr;
+            c = u - m * ppr;
+            const f32x4* src = reinterpret_cast<const f32x4*>(h + static_cast<size_t>(m) * K + ksl * KR + c * 8);
+            const f32x4 a0 = src[0], a1 = src[1];
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = e < 4 ? a0[e] : a1[e - 4];
+                hi[e] = __float_as_uint(v) & 0xffff0000u;   // truncation: the exact top half
+                const float rem = v - __uint_as_float(hi[e]);
+                lo[e] = __float_as_uint(rem) & 0xffff0000u;
+                sum += __uint_as_float(hi[e]) + __uint_as_float(lo[e]);
+            }
+            u32x4 oh, ol;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // element pairs (2i, 2i+1), or (i, i+4) for 4-bit codes
+                const int ea = BITS == 4 ? i : 2 * i, eb = BITS == 4 ? i + 4 : 2 * i + 1;
+                oh[i] = pack2(hi[ea], hi[eb]);
+                ol[i] = pack2(lo[ea], lo[eb]);
+            }
+            *reinterpret_cast<u32x4*>(xh + m * ldx + c * 8) = oh;
+            *reinterpret_cast<u32x4*>(xl + m * ldx + c * 8) = ol;
+        }
+#pragma unroll
+        for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
+        if (u < npieces && c % CPF == 0) xsum[(c / CPF) * kRows + m] = sum;
+    }
+    for (int u = static_cast<int>(threadIdx.x); u < (KR / FG) * (kRows - m_rows); u += 64 * S * P) {
+        const int ch = u / (kRows - m_rows), m = m_rows + (u - ch * (kRows - m_rows));
+        xsum[ch * kRows + m] = 0.f;
+    }
+    __syncthreads();
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool arow = li < m_rows;
+
+    auto compute = [&](const Words& cw, int f) {
+        const int i = f / nkw, j = f - i * nkw;
+        if (t0 + i * GP >= ntiles) return;   // wave-uniform
+        if (j == 0 && i > 0) load_pairs(i);
+        const int kl = ks * kw + j * KBK;    // k-block start inside the staged slice
+        f32x4 pt[NF];
+#pragma unroll
+        for (int fc = 0; fc < NF; ++fc) pt[fc] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            const int ka = WIDE ? kl + L::LK * kq + 8 * t : kl + 32 * t + 8 * kq;
+            const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+            const u32x4 ah = arow ? *reinterpret_cast<const u32x4*>(xh + li * ldx + ka) : z;
+            const u32x4 al = arow ? *reinterpret_cast<const u32x4*>(xl + li * ldx + ka) : z;
+            const u32x4 b = SC::operand(SC::step(cw, t));
+#pragma unroll
+            for (int fc = 0; fc < NF; ++fc) {
+                if constexpr (!WIDE) {
+                    if (t != fc) continue;
+                }
+                u32x4 th = ah, tl = al;
+                if constexpr (WIDE && NF > 1) {
+                    if ((kq * L::LK) / FG != fc) th = tl = z;
+                }
+                pt[fc] = mma<DT_BF16>(th, b, pt[fc]);
+                pt[fc] = mma<DT_BF16>(tl, b, pt[fc]);
+            }
+        }
+#pragma unroll
+        for (int fc = 0; fc < NF; ++fc) {
+            const f32x4 xc = *reinterpret_cast<const f32x4*>(xsum + (kl / FG + fc) * kRows + 4 * kq);
+            const f32x2 pv = pair_of((j * KBK + fc * FG) / G);
+            const float se = pv.x * SC::kInvMul, be = fmaf(-SC::kOff, se, pv.y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(se, pt[fc][e], fmaf(be, xc[e], acc[e]));
+        }
+    };
+
+    auto combine = [&](int i) {
+        if constexpr (S > 1) {
+            if (ks > 0) comb[ks - 1][p][lane] = acc;
+            __syncthreads();
+        }
+        const int tile = t0 + i * GP;
+        if (ks == 0 && tile < ntiles) {
+#pragma unroll
+            for (int s2 = 0; s2 < S - 1; ++s2) {
+                const f32x4 o = comb[s2][p][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += o[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 4 * kq + e;
+                if (m < m_rows) part[(static_cast<size_t>(ksl) * m_rows + m) * N + tile * kRows + li] = acc[e];
+            }
+        }
+        if constexpr (S > 1) __syncthreads();
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    for (int f0 = 0; f0 < nflat; f0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int f = f0 + u;
+            if (f < nflat) {
+                compute(st[u], f);
+                if (f + U < nflat) issue(st[u], f + U);
+                if ((f + 1) % nkw == 0) combine(f / nkw);
+            }
+        }
+    }
+}
+
+// y[m][n] = r[m][n] + sum over slices s (in order) of part[s][m][n]
+template <int ODT>
+__global__ void __launch_bounds__(256)
+qmm_down_reduce_kernel(const float* __restrict__ part, const void* __restrict__ r, void* __restrict__ out, int N,
+                       int m_rows, int NS) {
+    const int idx = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+    if (idx >= m_rows * N) return;
+    float acc = 0.f;
+    for (int s = 0; s < NS; ++s) acc += part[static_cast<size_t>(s) * m_rows * N + idx];
+    store_elem<ODT>(out, idx, load_elem<ODT>(r, idx) + acc);
+}
+
+// Slice length KR and tile groups per slice TB.  A wave's range (KR / S) is
+// a multiple of the k-block and of two groups and fits the pair registers, and
+// the staged slice fits LDS: the longest such slice (fewest partials, longest
+// k-run per tile).  Each slice gets the fewest tile groups that still give one
+// block per CU (all of them if the CUs cannot be covered).
+struct DownSplit { int kr, tb; };
+
+template <int BITS, int G>
+bool pick_down_split(int m, int n, int k, int cus, DownSplit& out) {
+    const int kbk = BlockLayout<BITS, G>::KBK;
+    const int unit = kbk > 2 * G ? kbk : 2 * G;   // both are powers of two
+    const int pw_max = 8 * pair_regs<G>() * G;
+    const size_t cap = kLdsCap - static_cast<size_t>(kDS > 1 ? kDS - 1 : 1) * kDP * 64 * 16;
+    const int groups = (n / kRows + kDP - 1) / kDP;
+    bool found = false;
+    for (int pw = unit; pw <= pw_max; pw += unit) {
+        const int kr = kDS * pw;
+        if (k % kr != 0 || down_lds_bytes<BITS, G>(m, kr) > cap) continue;
+        const int ns = k / kr;
+        out = {kr, std::min(groups, (cus + ns - 1) / ns)};
+        found = true;
+    }
+    return found;
+}
+
+// Partials of one stream's calls, per (device, stream), grown on demand.
+float* down_scratch(size_t bytes, hipStream_t s, int& err) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, hipStream_t>, std::pair<void*, size_t>> bufs;
+    err = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        err = static_cast<int>(hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    auto& b = bufs[std::make_tuple(dev, s)];
+    if (b.second >= bytes) return static_cast<float*>(b.first);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        err = static_cast<int>(hipErrorStreamCaptureUnsupported);   // first call must not be captured
+        return nullptr;
+    }
+    if (b.first) {
+        const hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) {
+            err = static_cast<int>(e);
+            return nullptr;
+        }
+        hipFree(b.first);
+        b = {nullptr, 0};
+    }
+    void* p = nullptr;
+    const hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        err = static_cast<int>(e);
+        return nullptr;
+    }
+    b = {p, bytes};
+    return static_cast<float*>(p);
+}
+
+template <int BITS, int G, int ODT>
+int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s) {
+    constexpr int NT = 64 * kDS * kDP;
+    constexpr int U = BlockLayout<BITS, G>::KBK == 128 ? kDU / 2 : kDU;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return static_cast<int>(hipErrorInvalidDevice);
+    DownSplit sp;
+    if (!pick_down_split<BITS, G>(m, w.n, w.k, cus, sp)) return static_cast<int>(hipErrorInvalidValue);
+    const int ns = w.k / sp.kr;
+    int err = 0;
+    float* part = down_scratch(static_cast<size_t>(ns) * m * w.n * sizeof(float), s, err);
+    if (!part) return err;
+    auto kern = qmm_down_part_kernel<BITS, G, kDS, kDP, U, pair_regs<G>()>;
+    const size_t lds = down_lds_bytes<BITS, G>(m, sp.kr);
+    if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+        return static_cast<int>(hipErrorInvalidValue);
+    hipError_t e = launch(kern, dim3(ns * sp.tb), dim3(NT), lds, s, static_cast<const uint8_t*>(w.q), w.scale_bias, h,
+                          part, w.n, w.k, sp.kr, sp.tb, m);
+    if (e != hipSuccess) return static_cast<int>(e);
+    const int outs = m * w.n;
+    e = launch(qmm_down_reduce_kernel<ODT>, dim3((outs + 255) / 256), dim3(256), 0, s,
+               static_cast<const float*>(part), r, out, w.n, m, ns);
+    return static_cast<int>(e);
+}
+
+template <int BITS, int ODT>
+int run_down_g(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s) {
+    switch (w.group) {
+        case 32: return run_down<BITS, 32, ODT>(w, h, r, out, m, s);
+        case 64: return run_down<BITS, 64, ODT>(w, h, r, out, m, s);
+        default: return run_down<BITS, 128, ODT>(w, h, r, out, m, s);
+    }
+}
+
+template <int ODT>
+int run_down_b(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s) {
+    return w.bits == 8 ? run_down_g<8, ODT>(w, h, r, out, m, s) : run_down_g<4, ODT>(w, h, r, out, m, s);
+}
+
+template <int BITS, int G>
+bool split_exists(int m, int n, int k) {
+    DownSplit sp;
+    return pick_down_split<BITS, G>(m, n, k, 1, sp);
+}
+
+}  // namespace
+
+bool mma_stream_down_supported(const qdm_weight& w, int m, int act) {
+    if (m < 2 || m > kRows) return false;
+    if (w.bits != 8 && w.bits != 4) return false;
+    if (w.group != 32 && w.group != 64 && w.group != 128) return false;
+    if (act != DT_BF16 && act != DT_F16) return false;   // h enters at ~16 bits: 16-bit outputs only
+    if (w.n % kRows != 0) return false;
+    if (w.bits == 4)
+        return w.group == 32 ? split_exists<4, 32>(m, w.n, w.k)
+             : w.group == 64 ? split_exists<4, 64>(m, w.n, w.k) : split_exists<4, 128>(m, w.n, w.k);
+    return w.group == 32 ? split_exists<8, 32>(m, w.n, w.k)
+         : w.group == 64 ? split_exists<8, 64>(m, w.n, w.k) : split_exists<8, 128>(m, w.n, w.k);
+}
+
+int launch_down_mma_stream(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
+                           void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return act == DT_F16 ? run_down_b<DT_F16>(dn, h, r, out, m, s) : run_down_b<DT_BF16>(dn, h, r, out, m, s);
+}
+
+}  // namespace qdm

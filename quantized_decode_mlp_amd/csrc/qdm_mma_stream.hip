@@ -35,135 +35,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "qdm_device.h"
 #include "qdm_internal.h"
 #include "qdm_launch.h"
+#include "qdm_mma_common.h"
 
 namespace qdm {
 namespace {
-
-typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kRows = 16;     // rows of the matrix tile
-constexpr int kPad = 8;       // f16 padding per staged row: 16 bytes, four LDS banks per row
-constexpr int kLdsCap = 160 * 1024;
-
-// 16x16x32 MMA in the activations' 16-bit type (bf16 or f16 operands)
-template <int XDT>
-__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-    if constexpr (XDT == DT_BF16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                       0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8, a), __builtin_bit_cast(h16x8, b), c, 0,
-                                                      0, 0);
-}
-
-// The eight codes of one lane and k-step as exact operand values off + c / inv
-// in the MMA's 16-bit type.  8-bit codes: f16 1024 + c (the byte under the
-// exponent byte 0x64, one permute per two codes) or the bf16 integer c (an
-// exact byte conversion and a permute of the high halves; no offset).  4-bit
-// codes: 1 + c/16 in either type (the nibble in the top mantissa bits of 1.0,
-// a shift and an and-or per two codes); element pairs (e, e + 4), so the
-// staged activations take that order too.
-template <int BITS, int XDT>
-struct StepCodes;
-
-template <int BITS>
-struct StepWords;
-
-template <>
-struct StepWords<8> {
-    using raw = u32x2;   // codes k + 0..7, one byte each
-    template <class W>
-    __device__ __forceinline__ static raw step(const W& w, int t) { return u32x2{w[2 * t], w[2 * t + 1]}; }
-    template <class W>
-    __device__ __forceinline__ static void set_step(W& w, int t, raw r) {
-        w[2 * t] = r[0];
-        w[2 * t + 1] = r[1];
-    }
-};
-
-template <>
-struct StepWords<4> {
-    using raw = uint32_t;   // codes k + 0..7, low nibble first
-    template <class W>
-    __device__ __forceinline__ static raw step(const W& w, int t) { return w[t]; }
-    template <class W>
-    __device__ __forceinline__ static void set_step(W& w, int t, raw r) { w[t] = r; }
-};
-
-template <>
-struct StepCodes<8, DT_F16> : StepWords<8> {
-    static constexpr float kOff = 1024.f, kInvMul = 1.f;
-    __device__ __forceinline__ static u32x4 operand(raw w) {
-        return u32x4{__builtin_amdgcn_perm(0x64646464u, w[0], 0x04010400u),
-                     __builtin_amdgcn_perm(0x64646464u, w[0], 0x04030402u),
-                     __builtin_amdgcn_perm(0x64646464u, w[1], 0x04010400u),
-                     __builtin_amdgcn_perm(0x64646464u, w[1], 0x04030402u)};
-    }
-};
-
-template <>
-struct StepCodes<8, DT_BF16> : StepWords<8> {
-    static constexpr float kOff = 0.f, kInvMul = 1.f;
-    // element 0 (low half) = a, element 1 = b, both exact bf16 values
-    __device__ __forceinline__ static uint32_t pack_hi(float a, float b) {
-        return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-    }
-    __device__ __forceinline__ static u32x4 operand(raw w) {
-        auto byte = [](uint32_t v, int i) { return static_cast<float>((v >> (8 * i)) & 0xffu); };
-        return u32x4{pack_hi(byte(w[0], 0), byte(w[0], 1)), pack_hi(byte(w[0], 2), byte(w[0], 3)),
-                     pack_hi(byte(w[1], 0), byte(w[1], 1)), pack_hi(byte(w[1], 2), byte(w[1], 3))};
-    }
-};
-
-template <>
-struct StepCodes<4, DT_F16> : StepWords<4> {
-    static constexpr float kOff = 1.f, kInvMul = 16.f;
-    // mantissa bits 9..6 of f16 1.0
-    __device__ __forceinline__ static u32x4 operand(raw w) {
-        return u32x4{((w << 6) & 0x03c003c0u) | 0x3c003c00u, ((w << 2) & 0x03c003c0u) | 0x3c003c00u,
-                     ((w >> 2) & 0x03c003c0u) | 0x3c003c00u, ((w >> 6) & 0x03c003c0u) | 0x3c003c00u};
-    }
-};
-
-template <>
-struct StepCodes<4, DT_BF16> : StepWords<4> {
-    static constexpr float kOff = 1.f, kInvMul = 16.f;
-    // mantissa bits 6..3 of bf16 1.0
-    __device__ __forceinline__ static u32x4 operand(raw w) {
-        return u32x4{((w << 3) & 0x00780078u) | 0x3f803f80u, ((w >> 1) & 0x00780078u) | 0x3f803f80u,
-                     ((w >> 5) & 0x00780078u) | 0x3f803f80u, ((w >> 9) & 0x00780078u) | 0x3f803f80u};
-    }
-};
-
-// k-block layout.  WIDE (groups of 64 or more): a k-block is KBK k, lane kq
-// holds the LK = KBK/4 consecutive k from LK*kq (one 16-byte load per row),
-// k-step t takes its codes 8t .. 8t+7; a block spanning NF > 1 groups runs
-// each step once per group with the activation kept only on that group's
-// lanes.  Otherwise (32-wide groups) a k-block is 64 k, lane kq holds k
-// 32t + 8kq .. +7 of step t (one load per step) and each step is one group.
-template <int BITS, int G>
-struct BlockLayout {
-    static constexpr bool WIDE = G >= 64;
-    static constexpr int KBK = (BITS == 4 && WIDE) ? 128 : 64;
-    static constexpr int STEPS = KBK / 32;
-    static constexpr int LK = KBK / 4;
-    static constexpr int FG = WIDE ? (G < KBK ? G : KBK) : 32;   // fold chunk (k)
-    static constexpr int NF = KBK / FG;                           // fold chunks per k-block
-    using Words = typename std::conditional<WIDE || BITS == 8, u32x4, u32x2>::type;
-};
-
-__host__ __device__ constexpr size_t round16(size_t v) { return (v + 15) & ~static_cast<size_t>(15); }
 
 // Dynamic LDS of the gate/up kernel: staged rows, then the fold-chunk sums.
 template <int BITS, int G>
@@ -419,10 +297,6 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
 
 // Block shape: S waves along K per tile, P tiles per block, U k-blocks in flight.
 constexpr int kS = 4, kP = 4, kU = 4;
-// pair registers per row set (8 groups each): the groups of one wave and tile
-// for K up to 8192 at 64- and 128-wide groups, 4096 at 32-wide ones
-template <int G>
-constexpr int pair_regs() { return G == 32 ? 4 : 2; }
 
 template <int BITS, int XDT, int G>
 int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s) {
