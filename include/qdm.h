@@ -22,8 +22,9 @@
  *     is launched or written: on error no output byte is touched.
  *   - Pointers named "device" are device (HBM) addresses owned by the
  *     caller; "host" pointers are ordinary host memory owned by the caller.
- *     The library never allocates, frees or synchronizes device memory and
- *     keeps no global state; calls are thread-safe.
+ *     The library's only device allocation and only global state is the
+ *     scratch of the few-row down projection (see qdm_gemv_down_residual);
+ *     calls are thread-safe.
  *   - GPU work is enqueued on `stream` (a hipStream_t; NULL = the legacy
  *     default stream) and the call returns without waiting.  A failed
  *     launch returns QDM_ERR_HIP.
@@ -162,14 +163,24 @@ int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act,
 /* out[m][d] = r + h W_down^T, fp32 accumulation, the residual added in fp32 and
  * the sum rounded once (nearest-even) to the act dtype.
  *   h     device fp32 [m][ffn];  r, out: device, act dtype, [m][d]
- *   down  descriptor with n = d, k = ffn.   out may not alias h; it may alias r. */
+ *   down  descriptor with n = d, k = ffn.   out may not alias h; it may alias r.
+ * With 2..16 rows, 8/4-bit weights and a 16-bit act dtype the sum is split
+ * along ffn across thread blocks: the partial sums go to a scratch buffer that
+ * the library allocates on the device at the first such call and keeps for the
+ * process (growing it, after a device-wide synchronize, when a larger call
+ * comes).  The allocating call must not be made while a stream is being
+ * captured into a graph (it then returns QDM_ERR_HIP): warm the largest shape
+ * up first.  All streams of a device share the buffer, so such calls that
+ * could run at the same time on different streams of one device must be
+ * ordered by the caller. */
 int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype act,
                            const qdm_weight* down, void* out, void* stream);
 
 /* The whole MLP: the two launches above on one stream, h kept in `workspace`
  * (device, >= qdm_mlp_workspace_bytes(m, ffn) bytes, 16-byte aligned).
  * gate_up->k must equal down->n (= d) and gate_up->n must equal down->k (= ffn);
- * both descriptors must use the same bits. */
+ * both descriptors must use the same bits.  The down half keeps its partial
+ * sums in the library's device scratch as qdm_gemv_down_residual does. */
 int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
                    const qdm_weight* gate_up, const qdm_weight* down,
                    void* workspace, size_t workspace_bytes, void* out, void* stream);

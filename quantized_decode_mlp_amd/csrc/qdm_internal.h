@@ -22,7 +22,7 @@ int launch_down_mma(const float* h, const void* r, int m, int act, const qdm_wei
 bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act);
 int launch_gate_up_mma_stream(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream);
 // 2..16 rows, 8/4-bit affine weights, 16-bit output: K split across blocks
-// with the partials in a per-stream scratch the library allocates on first use
+// with the partials in a device scratch the library allocates on first use
 // (qdm_mma_down.hip).
 bool mma_stream_down_supported(const qdm_weight& w, int m, int act);
 int launch_down_mma_stream(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,

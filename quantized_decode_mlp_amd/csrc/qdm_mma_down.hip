@@ -13,7 +13,7 @@
 // fold chunk, then streams 16-row weight tiles of that slice through
 // v_mfma_f32_16x16x32_bf16 (two MMAs per k-step, hi and lo) with the codes as
 // exact operands and each chunk's partial folded as in the gate/up kernel;
-// the partial tile goes to part[s][m][n].  Kernel 2 adds the NS partials in
+// the partial tile goes to part[s][m][n] (a scratch buffer of the device).  Kernel 2 adds the NS partials in
 // slice order and the residual and rounds to the output type.  Work split,
 // lane layout and scale/bias handling match the gate/up kernel: S waves take
 // contiguous quarters of a tile's k-range in the slice, P tiles per block,
@@ -287,10 +287,12 @@ bool pick_down_split(int m, int n, int k, int cus, DownSplit& out) {
     return found;
 }
 
-// Partials of one stream's calls, per (device, stream), grown on demand.
+// Partials scratch, one per device, grown on demand.  Growth happens only
+// outside graph capture and after the device has drained, since work on any
+// stream may still use the old buffer.
 float* down_scratch(size_t bytes, hipStream_t s, int& err) {
     static std::mutex mu;
-    static std::map<std::tuple<int, hipStream_t>, std::pair<void*, size_t>> bufs;
+    static std::map<int, std::pair<void*, size_t>> bufs;
     err = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
@@ -298,15 +300,15 @@ float* down_scratch(size_t bytes, hipStream_t s, int& err) {
         return nullptr;
     }
     std::lock_guard<std::mutex> lk(mu);
-    auto& b = bufs[std::make_tuple(dev, s)];
+    auto& b = bufs[dev];
     if (b.second >= bytes) return static_cast<float*>(b.first);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-        err = static_cast<int>(hipErrorStreamCaptureUnsupported);   // first call must not be captured
+        err = static_cast<int>(hipErrorStreamCaptureUnsupported);
         return nullptr;
     }
     if (b.first) {
-        const hipError_t e = hipStreamSynchronize(s);
+        const hipError_t e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             err = static_cast<int>(e);
             return nullptr;

@@ -197,6 +197,37 @@ def test_rows_are_independent(bits, group):
 
 # ------------------------------------------------------------------ special cases (bitwise)
 
+@pytest.mark.parametrize("m", [4, 16])
+@pytest.mark.parametrize("bits,group", [(4, 64), (8, 128)])
+def test_rows_graph_replay(m, bits, group):
+    """A few-row MLP captured into a HIP graph after one eager call (which
+    sizes the down projection's scratch) replays bitwise equal to the eager
+    result, with other work between replays, and meets the oracle bar."""
+    qdm = _qdm()
+    d, ffn = 1024, 1536
+    ow, (gu, dn) = generic_case((91, bits, m), d, ffn, bits, group)
+    x = W.generic_act((m, 8), (m, d), "bf16")
+    r = W.generic_act((m, 9), (m, d), "bf16")
+    xd, rd = to_device(x), to_device(r)
+    ws = torch.empty(qdm.mlp_workspace_bytes(m, ffn), dtype=torch.uint8, device="cuda")
+    y_eager = qdm.mlp_decode(xd, rd, gu, dn, workspace=ws).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(rd)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qdm.mlp_decode(xd, rd, gu, dn, workspace=ws, out=out)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, y_eager)
+    _, y_ref = oracle.mlp_decode(x.values, r.values, ow.wg, ow.wu, ow.wd)
+    ey = oracle.scaled_error(from_device(out), y_ref)
+    print(f"  y err {ey:.3e}", flush=True)
+    assert ey <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("wl_index", [1, 2, 5])
 def test_zero_input_gives_residual(wl_index):
     qdm = _qdm()
