@@ -157,9 +157,10 @@ def pcts(v):
             "p90": round(float(np.percentile(v, 90)), 3)}
 
 
-def other_configs(samples):
+def other_configs(samples, only=None):
     """The other workloads' decode MLP (and the add+RMSNorm row), each over address-distinct
-    weight copies of at least 2 GiB so no weight byte is served from a cache."""
+    weight copies of at least 2 GiB so no weight byte is served from a cache.  `only`
+    (workload index, rows) restricts it to that one MLP, e.g. for a kernel profile."""
     import torch
     import quantized_decode_mlp_amd as qdm
     res = {}
@@ -170,7 +171,7 @@ def other_configs(samples):
             torch.from_numpy(a.raw.view(np.int16)).view(torch_dt[a.dtype])
         return t.cuda()
 
-    for wi in (2, 3, 5):
+    for wi in ((only[0],) if only else (2, 3, 5)):
         wl = W.WORKLOADS[wi]
         g32, u32, d32 = W.weights_f32(wl, 0)
         if wl.bits == 16:
@@ -183,7 +184,7 @@ def other_configs(samples):
         copies = int(-(-(2 << 30) // wl.weight_bytes))
         sets = [(qdm.Weight.from_host(wl.ffn, wl.d, wl.bits, wl.group, q, sb),
                  qdm.Weight.from_host(wl.d, wl.ffn, wl.bits, wl.group, dq, dsb)) for _ in range(copies)]
-        for m in (wl.rows if wi == 5 else (1,)):
+        for m in ((only[1],) if only else (wl.rows if wi == 5 else (1,))):
             x, r = W.activations(wl, m)
             xd, rd = dev(x), dev(r)
             ws = torch.empty(qdm.mlp_workspace_bytes(m, wl.ffn), dtype=torch.uint8, device="cuda")
@@ -199,6 +200,8 @@ def other_configs(samples):
             _log(f"workload {wi} m={m}: {med:.2f} us/layer")
         del sets
         torch.cuda.empty_cache()
+    if only:
+        return res
     # add + RMSNorm (the row-a5 kernel) on the Llama-3.2-1B-shaped f16 row, and a launch floor
     wl = W.WORKLOADS[2]
     a, b, w = W.rmsnorm_inputs(wl)
@@ -284,6 +287,8 @@ def main(argv=None):
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--samples", type=int, default=20, help="graph-rotation samples for percentiles")
     ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--rows-only", type=int, default=0, metavar="M",
+                    help="only the Llama-3-8B-shaped MLP at M rows (graph replays), then exit")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args(argv)
@@ -300,6 +305,10 @@ def main(argv=None):
         print(json.dumps({"error": "no GPU visible"}))
         return 1
     torch.cuda.set_device(0)
+    if args.rows_only:
+        rec = other_configs(args.samples, only=(5, args.rows_only))
+        print(json.dumps({"workload": W.WORKLOADS[5].name, "rows": args.rows_only, **rec}))
+        return 0
     wl = W.WORKLOADS[4]
     n_layers = wl.n_sets
     sets = prepare_sets(wl, n_layers)

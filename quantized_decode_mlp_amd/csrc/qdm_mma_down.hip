@@ -257,9 +257,18 @@ qmm_down_reduce_kernel(const float* __restrict__ part, const void* __restrict__ 
                        int m_rows, int NS) {
     const int idx = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
     if (idx >= m_rows * N) return;
+    const size_t stride = static_cast<size_t>(m_rows) * N;
+    const float rv = load_elem<ODT>(r, idx);
+    // eight slices' loads in flight at a time, summed in slice order
     float acc = 0.f;
-    for (int s = 0; s < NS; ++s) acc += part[static_cast<size_t>(s) * m_rows * N + idx];
-    store_elem<ODT>(out, idx, load_elem<ODT>(r, idx) + acc);
+    for (int s0 = 0; s0 < NS; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = s0 + j < NS ? part[(s0 + j) * stride + idx] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += v[j];
+    }
+    store_elem<ODT>(out, idx, rv + acc);
 }
 
 // Slice length KR and tile groups per slice TB.  A wave's range (KR / S) is
