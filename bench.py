@@ -216,8 +216,8 @@ def other_configs(samples, only=None):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qwen3_8b_uint8_g128_mlp_hbm_counters.md")
-KERNEL_SOURCES = ["quantized_decode_mlp_amd/csrc/qdm_gemv.hip", "quantized_decode_mlp_amd/csrc/qdm_device.h",
-                  "quantized_decode_mlp_amd/csrc/qdm_launch.h"]
+KERNEL_SOURCES = ["quantized_decode_mlp_amd/csrc/qdm_gemv.hip", "quantized_decode_mlp_amd/csrc/qdm_stream.h",
+                  "quantized_decode_mlp_amd/csrc/qdm_device.h", "quantized_decode_mlp_amd/csrc/qdm_launch.h"]
 
 
 def measured_traffic():
@@ -364,6 +364,26 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
+    # the decode chain on the same 36 layer sets: add + RMSNorm then the MLP
+    # (three launches) against the chained call (two launches)
+    a, b, nw = W.chain_inputs(wl, 1)
+    ad, bd, nwd = (torch.from_numpy(v.raw.view(np.int16)).view(torch.bfloat16).cuda() for v in (a, b, nw))
+    so, no = torch.empty_like(ad), torch.empty_like(ad)
+    ws_c = torch.empty(qdm.mlp_rmsnorm_workspace_bytes(1, wl.d, wl.ffn, qdm.QDM_BF16), dtype=torch.uint8,
+                       device="cuda")
+
+    def sep(i):
+        qdm.add_rmsnorm(ad, bd, nwd, wl.norm_eps, s_out=so, n_out=no)
+        qdm.mlp_decode(no, so, *sets[i], workspace=ws, out=out)
+
+    t_sep = graph_samples(sep, n_layers, args.samples)
+    t_chain = graph_samples(lambda i: qdm.mlp_decode_rmsnorm(ad, bd, nwd, wl.norm_eps, *sets[i], workspace=ws_c,
+                                                             s_out=so, out=out), n_layers, args.samples)
+    chain = {"workload": "Qwen3-8B-shaped layer as above, with the residual add + RMSNorm (bf16, eps 1e-5) "
+                         "that feeds it",
+             "add_rmsnorm_then_mlp_us_per_layer": pcts(t_sep), "chained_us_per_layer": pcts(t_chain)}
+    _log(f"decode chain: {np.median(t_sep):.2f} us separate, {np.median(t_chain):.2f} us chained")
+
     others = None
     if not args.no_other_configs:
         others = other_configs(args.samples)
@@ -412,6 +432,7 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": gu_bytes,
         },
         "cpu_baseline": cpu,
+        "decode_chain": chain,
         "other_configs": others,
         "output_finite": finite,
     }

@@ -193,6 +193,33 @@ int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
 int qdm_add_rmsnorm(const void* a, const void* b, const void* w, int32_t rows, int32_t n,
                     float eps, qdm_dtype dtype, void* s_out, void* n_out, void* stream);
 
+/* Workspace bytes qdm_mlp_decode_rmsnorm needs: h[m][ffn] fp32 plus two
+ * [m][d] rows of the act dtype, each rounded up to 256 bytes; 0 if invalid. */
+size_t qdm_mlp_rmsnorm_workspace_bytes(int32_t m, int32_t d, int32_t ffn, qdm_dtype act);
+
+/* The decode chain across the layer boundary: the residual add + RMSNorm
+ * above feeding the MLP, with the sum as the MLP's residual ("Compute-Graph
+ * Fusion": the GraphBuilder example's add + RMSNorm with the sum kept, and
+ * the gated MLP with the residual added in the down projection):
+ *   s = a + b (rounded once),  n = s * w / sqrt(mean(s^2) + eps) (rounded once),
+ *   out = s + W_down (silu(W_gate n) * (W_up n)).
+ * Results are bitwise those of qdm_add_rmsnorm followed by qdm_mlp_decode
+ * with x = n and r = s.  With one row and shapes the one-row streaming
+ * kernels take, two launches: every gate/up block recomputes s, the mean
+ * square and n from a, b and w, and the down launch adds s as its residual
+ * (n and s never go to HBM).  Otherwise the three launches run in order
+ * through the workspace.
+ *   a, b     device, act dtype, [m][d]; out may alias either.
+ *   norm_w   device, act dtype, [d];  eps >= 0 and finite.
+ *   s_out    device, act dtype, [m][d], or NULL (s not written); may alias
+ *            a or b, not out.
+ *   workspace device, >= qdm_mlp_rmsnorm_workspace_bytes(m, d, ffn, act)
+ *            bytes, 16-byte aligned, overlapping no other argument.
+ *   Weights as for qdm_mlp_decode (gate_up->k = down->n = d, same bits). */
+int qdm_mlp_decode_rmsnorm(const void* a, const void* b, const void* norm_w, float eps, int32_t m, qdm_dtype act,
+                           const qdm_weight* gate_up, const qdm_weight* down,
+                           void* workspace, size_t workspace_bytes, void* s_out, void* out, void* stream);
+
 /* ----------------------------------------------------------------- misc */
 
 /* A static string naming a status code. */

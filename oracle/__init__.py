@@ -17,6 +17,9 @@ What it computes (plain definitions, numpy, float64):
   "MLX-LM Backend" page, section "Dispatch Policy", typed residual store).
 * ``add_rmsnorm`` -- s = a + b, n = rms_norm(s, w, eps), both returned
   ("Compute-Graph Fusion" page, opening GraphBuilder example).
+* ``mlp_decode_rmsnorm`` -- the decode chain: add + RMSNorm feeding the MLP,
+  the sum as its residual ("Compute-Graph Fusion" page, GraphBuilder example
+  and "Automatic Gated Epilogues").
 * ``scaled_error`` -- max|out - ref| / max|ref|, the scale-normalized error
   ("Compute-Graph Fusion" page, section "Automatic Gated Epilogues").
 
@@ -30,6 +33,7 @@ from .pack import (pack_codes, unpack_codes, pack_scale_bias, unpack_scale_bias,
                    pack_gate_up, pack_gate_up_scale_bias, pack_dense_gate_up)
 from .mlp import silu, gate_up_swiglu, down_residual, mlp_decode
 from .rmsnorm import round_to_dtype, add_rmsnorm
+from .chain import mlp_decode_rmsnorm
 from .compare import scaled_error
 
 __all__ = [
@@ -37,5 +41,5 @@ __all__ = [
     "pack_codes", "unpack_codes", "pack_scale_bias", "unpack_scale_bias",
     "pack_gate_up", "pack_gate_up_scale_bias", "pack_dense_gate_up",
     "silu", "gate_up_swiglu", "down_residual", "mlp_decode",
-    "round_to_dtype", "add_rmsnorm", "scaled_error",
+    "round_to_dtype", "add_rmsnorm", "mlp_decode_rmsnorm", "scaled_error",
 ]

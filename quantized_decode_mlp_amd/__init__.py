@@ -33,7 +33,8 @@ EXPORTS = (
     "qdm_quantize_affine", "qdm_pack_rows", "qdm_quantize_pack_rows",
     "qdm_quantize_pack_gate_up", "qdm_pack_gate_up", "qdm_pack_dense_gate_up",
     "qdm_gemv_gate_up_swiglu", "qdm_gemv_down_residual", "qdm_mlp_decode",
-    "qdm_add_rmsnorm", "qdm_status_string", "qdm_version",
+    "qdm_add_rmsnorm", "qdm_mlp_rmsnorm_workspace_bytes", "qdm_mlp_decode_rmsnorm",
+    "qdm_status_string", "qdm_version",
 )
 
 
@@ -73,6 +74,9 @@ def _load():
         "qdm_mlp_decode": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
                                           ctypes.POINTER(qdm_weight), vp, sz, vp, vp]),
         "qdm_add_rmsnorm": (ctypes.c_int, [vp, vp, vp, i32, i32, f32, ctypes.c_int, vp, vp, vp]),
+        "qdm_mlp_rmsnorm_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int]),
+        "qdm_mlp_decode_rmsnorm": (ctypes.c_int, [vp, vp, vp, f32, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
+                                                  ctypes.POINTER(qdm_weight), vp, sz, vp, vp, vp]),
         "qdm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "qdm_version": (ctypes.c_int, []),
     }
@@ -110,6 +114,10 @@ def scale_bias_floats(n: int, k: int, group: int) -> int:
 
 def mlp_workspace_bytes(m: int, ffn: int) -> int:
     return int(_lib.qdm_mlp_workspace_bytes(m, ffn))
+
+
+def mlp_rmsnorm_workspace_bytes(m: int, d: int, ffn: int, dtype: int) -> int:
+    return int(_lib.qdm_mlp_rmsnorm_workspace_bytes(m, d, ffn, dtype))
 
 
 # ------------------------------------------------------------------ host: quantize / pack
@@ -320,9 +328,34 @@ def add_rmsnorm(a, b, w, eps: float, s_out=None, n_out=None, stream=None):
     return s_out, n_out
 
 
+def mlp_decode_rmsnorm(a, b, norm_w, eps: float, gate_up: Weight, down: Weight, workspace=None, s_out=None,
+                       out=None, stream=None):
+    """The decode chain: s = a + b, n = rmsnorm(s) * norm_w, out = s + MLP(n);
+    a, b, out [m, d], norm_w [d], one dtype.  s goes to s_out when given."""
+    torch = _torch()
+    if not (a.dtype == b.dtype == norm_w.dtype):
+        raise TypeError("a, b and norm_w must share a dtype")
+    m = a.shape[0] if a.dim() == 2 else 1
+    ws_bytes = mlp_rmsnorm_workspace_bytes(m, gate_up.k, gate_up.n, _dt(a))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
+    if out is None:
+        out = torch.empty_like(a)
+    if out.dtype != a.dtype or (s_out is not None and s_out.dtype != a.dtype):
+        raise TypeError("out and s_out must have the dtype of a")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.qdm_mlp_decode_rmsnorm(_dev(a, "a"), _dev(b, "b"), _dev(norm_w, "norm_w"), float(eps), m, _dt(a),
+                                       ctypes.byref(gate_up.descriptor), ctypes.byref(down.descriptor),
+                                       _dev(workspace, "workspace"), nbytes,
+                                       None if s_out is None else _dev(s_out, "s_out"), _dev(out, "out"),
+                                       _stream(stream)), "qdm_mlp_decode_rmsnorm")
+    return out
+
+
 __all__ = [
     "Weight", "QdmError", "qdm_weight", "EXPORTS", "LIB_PATH",
     "status_string", "version", "packed_q_bytes", "scale_bias_floats", "mlp_workspace_bytes",
     "quantize_affine", "pack_rows", "quantize_pack_rows", "quantize_pack_gate_up", "pack_gate_up",
     "pack_dense_gate_up", "gemv_gate_up_swiglu", "gemv_down_residual", "mlp_decode", "add_rmsnorm",
+    "mlp_rmsnorm_workspace_bytes", "mlp_decode_rmsnorm",
 ]

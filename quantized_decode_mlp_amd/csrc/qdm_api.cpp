@@ -37,6 +37,10 @@ int check_rows(int32_t m) { return (m >= 1 && m <= kMaxRows) ? QDM_OK : (m < 1 ?
 
 int hip_status(int e) { return e == 0 ? QDM_OK : QDM_ERR_HIP; }
 
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t act_bytes(int dt) { return dt == QDM_F32 ? 4 : 2; }
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +89,46 @@ int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
     float* h = static_cast<float*>(workspace);
     if (int e = qdm::launch_gate_up_swiglu(x, m, act, *gate_up, h, stream)) return hip_status(e);
     return hip_status(qdm::launch_down_residual(h, r, m, act, *down, out, stream));
+}
+
+size_t qdm_mlp_rmsnorm_workspace_bytes(int32_t m, int32_t d, int32_t ffn, qdm_dtype act) {
+    if (m <= 0 || d <= 0 || ffn <= 0 || !valid_dtype(act)) return 0;
+    return round256(static_cast<size_t>(m) * static_cast<size_t>(ffn) * sizeof(float)) +
+           2 * round256(static_cast<size_t>(m) * static_cast<size_t>(d) * act_bytes(act));
+}
+
+int qdm_mlp_decode_rmsnorm(const void* a, const void* b, const void* norm_w, float eps, int32_t m, qdm_dtype act,
+                           const qdm_weight* gate_up, const qdm_weight* down,
+                           void* workspace, size_t workspace_bytes, void* s_out, void* out, void* stream) {
+    if (!a || !b || !norm_w || !out) return QDM_ERR_INVALID_ARG;
+    if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.0f) return QDM_ERR_INVALID_ARG;
+    if (int e = check_rows(m)) return e;
+    if (int e = check_weight(gate_up)) return e;
+    if (int e = check_weight(down)) return e;
+    if (gate_up->k != down->n || gate_up->n != down->k) return QDM_ERR_INVALID_ARG;
+    if (gate_up->bits != down->bits) return QDM_ERR_UNSUPPORTED;
+    const int32_t d = gate_up->k, ffn = gate_up->n;
+    if (!workspace || workspace_bytes < qdm_mlp_rmsnorm_workspace_bytes(m, d, ffn, act)) return QDM_ERR_WORKSPACE;
+    if (s_out == out) return QDM_ERR_INVALID_ARG;
+    if (workspace == out || workspace == s_out || workspace == a || workspace == b) return QDM_ERR_INVALID_ARG;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(norm_w, 16) || !aligned(out, 16) ||
+        !aligned(s_out, 16) || !aligned(workspace, 16))
+        return QDM_ERR_ALIGNMENT;
+    float* h = static_cast<float*>(workspace);
+    if (m == 1 && qdm::chain_stream_supported(*gate_up, *down, act))
+        return hip_status(qdm::launch_mlp_chain_stream(a, b, norm_w, eps, act, *gate_up, *down, h, s_out, out,
+                                                       stream));
+    // otherwise the three launches: add + RMSNorm into the workspace (s into
+    // s_out when given), then the MLP on n with s as the residual
+    char* base = static_cast<char*>(workspace);
+    const size_t hb = round256(static_cast<size_t>(m) * static_cast<size_t>(ffn) * sizeof(float));
+    const size_t vb = round256(static_cast<size_t>(m) * static_cast<size_t>(d) * act_bytes(act));
+    void* n_buf = base + hb;
+    void* s_buf = s_out ? s_out : static_cast<void*>(base + hb + vb);
+    if (int e = qdm::launch_add_rmsnorm(a, b, norm_w, m, d, eps, act, s_buf, n_buf, stream)) return hip_status(e);
+    if (int e = qdm::launch_gate_up_swiglu(n_buf, m, act, *gate_up, h, stream)) return hip_status(e);
+    return hip_status(qdm::launch_down_residual(h, s_buf, m, act, *down, out, stream));
 }
 
 int qdm_add_rmsnorm(const void* a, const void* b, const void* w, int32_t rows, int32_t n,

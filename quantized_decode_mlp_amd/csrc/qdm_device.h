@@ -51,6 +51,14 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
     else static_cast<uint16_t*>(p)[i] = f32_to_f16(v);
 }
 
+// v rounded once (nearest-even) to DT and back to fp32.
+template <int DT>
+__device__ __forceinline__ float round_trip(float v) {
+    if constexpr (DT == DT_F32) return v;
+    else if constexpr (DT == DT_BF16) return bf16_to_f32(f32_to_bf16(v));
+    else return f16_to_f32(f32_to_f16(v));
+}
+
 // Loads N consecutive elements (N * sizeof(elem) in {4, 8, 16, 32} bytes, aligned
 // to min(16, that size)) as fp32.
 template <int DT, int N>

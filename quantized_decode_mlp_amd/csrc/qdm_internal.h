@@ -27,6 +27,11 @@ int launch_gate_up_mma_stream(const void* x, int m, int act, const qdm_weight& g
 bool mma_stream_down_supported(const qdm_weight& w, int m, int act);
 int launch_down_mma_stream(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
                            void* stream);
+// One row, both projections on the streaming kernels: the decode chain with
+// add + RMSNorm folded into the MLP's two launches (qdm_chain.hip).
+bool chain_stream_supported(const qdm_weight& gu, const qdm_weight& dn, int act);
+int launch_mlp_chain_stream(const void* a, const void* b, const void* w, float eps, int act, const qdm_weight& gu,
+                            const qdm_weight& dn, float* h, void* s_out, void* out, void* stream);
 int launch_add_rmsnorm(const void* a, const void* b, const void* w, int rows, int n, float eps,
                        int dtype, void* s_out, void* n_out, void* stream);
 

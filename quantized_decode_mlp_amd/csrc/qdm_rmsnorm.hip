@@ -23,13 +23,6 @@ namespace {
 constexpr int kThreads = 256;
 
 template <int DT>
-__device__ __forceinline__ float round_trip(float v) {
-    if constexpr (DT == DT_F32) return v;
-    else if constexpr (DT == DT_BF16) return bf16_to_f32(f32_to_bf16(v));
-    else return f16_to_f32(f32_to_f16(v));
-}
-
-template <int DT>
 __global__ void __launch_bounds__(kThreads)
 add_rmsnorm_kernel(const void* a, const void* b, const void* __restrict__ w,
                    int n, float eps, void* s_out, void* __restrict__ n_out) {

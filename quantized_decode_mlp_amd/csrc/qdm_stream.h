@@ -1,0 +1,529 @@
+// One-row streaming GEMV kernel for gfx950 (gate/up with the SwiGLU epilogue,
+// down with the residual epilogue) and its host launchers, optionally with
+// the decode chain's residual add + RMSNorm folded in (CHAIN).  Included by
+// qdm_gemv.hip (plain projections) and qdm_chain.hip (the chained forms);
+// each translation unit instantiates what it launches.
+//
+// Pages: meTile docs, "Compute-Graph Fusion", section "Automatic Gated
+// Epilogues" (two projections sharing the activation, silu(gate) * up on chip,
+// residual added inside the one-row down projection) and the opening
+// GraphBuilder example (residual add feeding RMSNorm, the sum kept as an
+// output); "MLX-LM Backend", section "Dispatch Policy" (gate and up share each
+// activation load, SwiGLU before the only write of h, typed residual store,
+// RMSNorm accumulating in FP32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qdm_device.h"
+#include "qdm_internal.h"
+#include "qdm_launch.h"
+
+namespace qdm {
+
+// Inputs of the chained forms (unused otherwise).  Gate/up: the block's
+// activation row is n = rmsnorm(a + b) * w, recomputed in every block.  Down:
+// the residual is s = a + b (rounded once), optionally stored to s_out.
+struct ChainArgs {
+    const void* a;
+    const void* b;
+    const void* w;
+    void* s_out;
+    float eps;
+};
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// One-row streaming kernel.  Persistent blocks (as many as fit on the chip)
+// walk the outputs (a gate/up pair, or one down row) in rounds.  A block is P
+// independent row streams of S wave64s each; the S waves of a stream split
+// K: wave ks owns TW consecutive K-tiles, i.e. chunk c = (ks*TW + j)*64 +
+// lane for j < TW, and holds the matching fp32 activations (TW*E of them, at
+// most 64) and their sums in registers for the whole launch.
+//
+// The activation row is copied once per block into LDS (each thread moves a
+// few 16-byte pieces, issued before the first weight loads) and every wave
+// reads its slice from there: one copy per block instead of one per wave
+// through the vector-memory path, which a CU shares between all of its
+// waves (fp32 h is 4 bytes per 8-bit down code).
+//
+// Each round a wave loads its TW weight chunks of the round's row(s) and the
+// scale/bias pair of each chunk's group (non-temporal: weights are read
+// exactly once), reduces them, and only then issues the next round: one
+// round in flight per wave.  Deeper per-wave pipelines (two to six rounds,
+// with the CU's register file spent on them instead of on more waves)
+// measured slower on this part; so did loading a wave's pairs once and
+// spreading them with ds_bpermute (an LDS round trip on every round).  Loads
+// are unconditional: a lane past the end of a row or a stream past its last
+// row reads a clamped, valid address and its contribution is zeroed through
+// the activations (0 for such lanes) or not stored.  Row bases are wave-uniform
+// (scalar registers) and lane offsets 32-bit.  Wave totals come from DPP row
+// reductions; the split-K partials of up to kBatch rounds are parked in LDS
+// and combined in wave order after one barrier per batch, so results are
+// bitwise reproducible.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+
+template <int BITS>
+struct StreamShape {
+    static constexpr int E = 128 / BITS;                              // codes per 16-byte chunk
+    static constexpr int TW_MAX = 64 / E;                             // K-tiles per wave at most
+};
+
+constexpr int kBatch = 16;            // rounds whose split-K partials share one LDS combine
+constexpr int kStreamLds = 65536;     // largest activation row staged in LDS (bytes)
+
+template <int XDT>
+constexpr int x_bytes() { return XDT == DT_F32 ? 4 : 2; }
+
+// Stream (block b, p) takes groups b*P + p + i*G*P for rounds i = 0, 1, ...
+// (G = gridDim); every wave walks the same number of rounds, so the block's
+// barriers line up even when a stream has run out of groups.
+// Element-wise f over the activation-type values packed in two dwords (one
+// fp32 value, or two 16-bit values low half first); the results are rounded
+// once to the type and packed the same way.
+template <int DT, typename F>
+__device__ __forceinline__ uint32_t dword_map(uint32_t xa, uint32_t xb, F f) {
+    if constexpr (DT == DT_F32) {
+        return __float_as_uint(f(__uint_as_float(xa), __uint_as_float(xb)));
+    } else {
+        auto val = [](uint32_t h) { return DT == DT_BF16 ? bf16_to_f32(h) : f16_to_f32(h); };
+        auto bits = [](float v) -> uint32_t { return DT == DT_BF16 ? f32_to_bf16(v) : f32_to_f16(v); };
+        const uint32_t lo = bits(f(val(xa & 0xffffu), val(xb & 0xffffu)));
+        const uint32_t hi = bits(f(val(xa >> 16), val(xb >> 16)));
+        return lo | (hi << 16);
+    }
+}
+
+template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P, bool CHAIN>
+__global__ void __launch_bounds__(64 * S * P)
+qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
+                    const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
+                    int n_out, int k, int gshift, ChainArgs ch) {
+    constexpr int E = StreamShape<BITS>::E;
+    constexpr int EPD = E / 4;
+    constexpr int NV = GU ? 2 : 1;
+    constexpr bool AFFINE = BITS != 16;
+    constexpr int NT = 64 * S * P;
+    constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
+    constexpr bool NORM = CHAIN && GU;   // the activation row is rmsnorm(a + b) * w
+    constexpr int kNormThreads = 256;    // the standalone add + RMSNorm kernel's block
+    static_assert(!NORM || NT >= kNormThreads, "the norm prologue needs four waves");
+
+    extern __shared__ __align__(16) uint8_t xlds[];   // the activation row, k * x_bytes bytes
+    __shared__ float part[(S > 1) ? kBatch : 1][P][S][NV];
+    __shared__ float nred[NORM ? kNormThreads / 64 : 1];
+
+    const int lane = threadIdx.x & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler keep it scalar
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wv % S, p = wv / S;
+    const uint32_t rb = static_cast<uint32_t>(k) * BITS / 8;   // bytes per packed row
+    const int C = static_cast<int>(rb >> 4);
+    const int ng = AFFINE ? (k >> gshift) : 0;
+    const int GP = static_cast<int>(gridDim.x) * P;
+    const int g0 = static_cast<int>(blockIdx.x) * P + p;
+    const int rounds = (n_out - static_cast<int>(blockIdx.x) * P + GP - 1) / GP;   // same for every wave
+    if (rounds <= 0) return;   // uniform per block, before any barrier
+
+    // first pieces of the activation row (issued before the weights: the
+    // in-order load counter then lets them land without waiting for weights)
+    const int nunits = (k * x_bytes<XDT>()) >> 4;
+    const int tid = static_cast<int>(threadIdx.x);
+    const u32x4* xg = static_cast<const u32x4*>(NORM ? ch.a : xin);
+    u32x4* xl = reinterpret_cast<u32x4*>(xlds);
+    u32x4 xt[XU], bt, wt;
+    if constexpr (NORM) {
+        if (tid < nunits) {
+            xt[0] = xg[tid];
+            bt = static_cast<const u32x4*>(ch.b)[tid];
+            wt = static_cast<const u32x4*>(ch.w)[tid];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int idx = tid + u * NT;
+            if (idx < nunits) xt[u] = xg[idx];
+        }
+    }
+
+    // lane offsets (bytes) of this wave's chunks and of their scale/bias pairs,
+    // clamped into the row
+    uint32_t qoff[TW], soff[TW];
+    bool vj[TW];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+        const int c = (ks * TW + j) * 64 + lane;
+        vj[j] = c < C;
+        const uint32_t cc = static_cast<uint32_t>(vj[j] ? c : C - 1);
+        qoff[j] = cc * 16u;
+        soff[j] = AFFINE ? ((cc * E) >> gshift) * 8u : 0u;
+    }
+
+    u32x4 wbuf[NV][TW];
+    f32x2 pbuf[NV][TW];
+
+    // loads of group grp (rows clamped; a stream past its last group reloads row n_out - 1)
+    auto issue = [&](u32x4 (&wq)[NV][TW], f32x2 (&pp)[NV][TW], int grp) {
+        const uint32_t row = static_cast<uint32_t>(min(grp, n_out - 1));
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const uint32_t prow = GU ? 2u * row + v : row;
+            const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
+            const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * ng * 8u;
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                wq[v][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + qoff[j]));
+                if constexpr (AFFINE)
+                    pp[v][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + soff[j]));
+            }
+        }
+    };
+
+    // the first round goes in flight before the activations are set up
+    if (g0 < n_out) issue(wbuf, pbuf, g0);
+
+    if constexpr (NORM) {
+        // The decode chain's RMSNorm, recomputed by every block from a, b and w
+        // (L2-resident after the first blocks): s = a + b rounded once, staged
+        // in LDS; the mean square of s summed exactly as the standalone add +
+        // RMSNorm kernel does (its 256 threads' strided sums, wave sums, the
+        // four in order); then n = s * inv * w rounded once, in place.  n is
+        // therefore the value that kernel would store.
+        const u32x4* bg = static_cast<const u32x4*>(ch.b);
+        const u32x4* wg = static_cast<const u32x4*>(ch.w);
+        auto add_piece = [&](int idx, const u32x4 av, const u32x4 bv) {
+            u32x4 sv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t aw = av[i], bw = bv[i];
+                sv[i] = dword_map<XDT>(aw, bw, [](float x, float y) { return x + y; });
+            }
+            xl[idx] = sv;
+        };
+        if (tid < nunits) add_piece(tid, xt[0], bt);
+        for (int idx = tid + NT; idx < nunits; idx += NT) add_piece(idx, xg[idx], bg[idx]);
+        __syncthreads();
+        if (tid < kNormThreads) {
+            float ss = 0.f;
+            for (int i = tid; i < k; i += kNormThreads) {
+                const float sv = load_elem<XDT>(xlds, i);
+                ss = fmaf(sv, sv, ss);
+            }
+            ss = wave_sum(ss);
+            if ((tid & 63) == 0) nred[tid >> 6] = ss;
+        }
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < kNormThreads / 64; ++i) tot += nred[i];
+        const float inv = 1.0f / sqrtf(tot / static_cast<float>(k) + ch.eps);
+        auto norm_piece = [&](int idx, const u32x4 wv) {
+            const u32x4 sv = xl[idx];
+            u32x4 nv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t sw = sv[i], ww = wv[i];
+                nv[i] = dword_map<XDT>(sw, ww, [inv](float x, float y) { return x * inv * y; });
+            }
+            xl[idx] = nv;
+        };
+        if (tid < nunits) norm_piece(tid, wt);
+        for (int idx = tid + NT; idx < nunits; idx += NT) norm_piece(idx, wg[idx]);
+    } else {
+        // rest of the activation copy, then this wave's slice
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int idx = tid + u * NT;
+            if (idx < nunits) xl[idx] = xt[u];
+        }
+        for (int idx = tid + XU * NT; idx < nunits; idx += NT) xl[idx] = xg[idx];
+    }
+    __syncthreads();
+
+    // Dot-product form.  DM 0: fp32 activations, one FMA per code.  DM 1
+    // (8/4-bit codes, 16-bit activations): v_dot2_f32_f16 on two codes at a
+    // time.  A code becomes an exact f16 value by placing its bits in the
+    // mantissa under a fixed exponent: an 8-bit code c under the exponent
+    // byte 0x64 gives 1024 + c (one byte permute per two codes); a 4-bit
+    // code n in the top mantissa bits of 1.0 gives 1 + n/16 (a shift and an
+    // and-or per two codes), which keeps the offset small against the code.
+    // The activations are held as f16 after a per-lane power-of-two scale
+    // 2^sg that puts the lane's largest magnitude in [2^14, 2^15) (a bf16 or
+    // f16 value converts exactly unless it lies more than 2^28 below it); the
+    // offset's share (1024 or 1 times the chunk's scaled activation sum) is
+    // taken off per chunk before the group scale applies, and the powers of
+    // two come off once per row.  DM 2 (bf16 weights, bf16 activations):
+    // v_dot2_f32_bf16 straight on the packed words.
+    constexpr int DM = (AFFINE && XDT != DT_F32) ? 1 : (BITS == 16 && XDT == DT_BF16) ? 2 : 0;
+    float xv[TW][E];
+    float xs[TW];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+        xs[j] = 0.f;
+        const int c = (ks * TW + j) * 64 + lane;
+        if (vj[j]) {
+            load_vec<XDT, E>(xlds, static_cast<int64_t>(c) * E, xv[j]);
+            if constexpr (DM != 1) {   // DM 1 takes the sum from the f16 pairs below
+#pragma unroll
+                for (int e = 0; e < E; ++e) xs[j] += xv[j][e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) xv[j][e] = 0.f;
+        }
+    }
+    uint32_t xp[TW][DM == 0 ? 1 : E / 2];   // packed 16-bit activation pairs (DM 1, 2)
+    float xoff[TW];                         // DM 1: the offset's share of a chunk's dot product
+    int nsg = 0;                            // DM 1: -sg (+4 for 4-bit codes, which enter as n/16)
+    if constexpr (DM == 1) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < TW; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(xv[j][e]));
+        const int sg = 15 - __builtin_amdgcn_frexp_expf(m);
+        nsg = BITS == 8 ? -sg : 4 - sg;
+#pragma unroll
+        for (int j = 0; j < TW; ++j) {
+            _Float16 hv[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) hv[e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(xv[j][e], sg));
+            // pair order matches the code pairs built in finish(): 8-bit (4i+2h, 4i+2h+1),
+            // 4-bit (8i+e, 8i+e+4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int h = 0; h < E / 8; ++h) {
+                    const int a = BITS == 8 ? 4 * i + 2 * h : 8 * i + h;
+                    const int b = BITS == 8 ? a + 1 : a + 4;
+                    xp[j][i * (E / 8) + h] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[a])) |
+                                             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[b])) << 16);
+                }
+            }
+            // the chunk's scaled sum (pairs against 1.0), and the unscaled sum for the
+            // bias term: exact scalings of one another
+            float t = 0.f;
+#pragma unroll
+            for (int i = 0; i < E / 2; ++i)
+                t = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, xp[j][i]), __builtin_bit_cast(h16x2, 0x3c003c00u), t,
+                                           false);
+            xoff[j] = (BITS == 8 ? 1024.f : 1.f) * t;
+            xs[j] = __builtin_amdgcn_ldexpf(t, -sg);
+        }
+    } else if constexpr (DM == 2) {
+#pragma unroll
+        for (int j = 0; j < TW; ++j)
+#pragma unroll
+            for (int i = 0; i < E / 2; ++i)   // the activations are bf16 values: their fp32 high halves
+                xp[j][i] = (__float_as_uint(xv[j][2 * i]) >> 16) | (__float_as_uint(xv[j][2 * i + 1]) & 0xffff0000u);
+    }
+
+    auto epilogue = [&](int grp, const float (&t)[NV]) {
+        if constexpr (GU) {
+            const float gs = t[0];
+            static_cast<float*>(out)[grp] = gs / (1.0f + expf(-gs)) * t[NV - 1];
+        } else if constexpr (CHAIN) {
+            // the residual is the chain's sum s = a + b, rounded once as stored
+            const float sv = round_trip<ODT>(load_elem<ODT>(ch.a, grp) + load_elem<ODT>(ch.b, grp));
+            if (ch.s_out) store_elem<ODT>(ch.s_out, grp, sv);
+            store_elem<ODT>(out, grp, sv + t[0]);
+        } else {
+            store_elem<ODT>(out, grp, load_elem<ODT>(resid, grp) + t[0]);
+        }
+    };
+
+    // combines the parked partials of rounds first .. first+cnt-1 for every stream
+    auto combine = [&](int first, int cnt) {
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < cnt * P) {
+            const int slot = t / P, sp = t % P;
+            const int grp = static_cast<int>(blockIdx.x) * P + sp + (first + slot) * GP;
+            if (grp < n_out) {
+                float tot[NV];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int s2 = 0; s2 < S; ++s2) a += part[slot][sp][s2][v];
+                    tot[v] = a;
+                }
+                epilogue(grp, tot);
+            }
+        }
+        __syncthreads();
+    };
+
+    auto finish = [&](const u32x4 (&wq)[NV][TW], const f32x2 (&pp)[NV][TW], int grp, int slot) {
+        if (grp >= n_out) return;   // this stream is past its last group (wave-uniform)
+        float tot[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float acc = 0.f, acc2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                float dot = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t word = wq[v][j][i];
+                    if constexpr (DM == 1 && BITS == 8) {
+                        const uint32_t c01 = __builtin_amdgcn_perm(0x64646464u, word, 0x04010400u);
+                        const uint32_t c23 = __builtin_amdgcn_perm(0x64646464u, word, 0x04030402u);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c01), __builtin_bit_cast(h16x2, xp[j][2 * i]),
+                                                     dot, false);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c23),
+                                                     __builtin_bit_cast(h16x2, xp[j][2 * i + 1]), dot, false);
+                    } else if constexpr (DM == 1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            // nibbles e and e + 4 into mantissa bits 9..6 of the two halves
+                            const uint32_t sh = e < 2 ? word << (6 - 4 * e) : word >> (4 * e - 6);
+                            const uint32_t ce = (sh & 0x03c003c0u) | 0x3c003c00u;
+                            dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, ce),
+                                                         __builtin_bit_cast(h16x2, xp[j][4 * i + e]), dot, false);
+                        }
+                    } else if constexpr (DM == 2) {
+                        dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, word),
+                                                              __builtin_bit_cast(b16x2, xp[j][i]), dot, false);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPD; ++e) {
+                            float c;
+                            if constexpr (BITS == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
+                            else if constexpr (BITS == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
+                            else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
+                            dot = fmaf(c, xv[j][i * EPD + e], dot);
+                        }
+                    }
+                }
+                if constexpr (AFFINE) {
+                    const float sc = pp[v][j].x, bi = pp[v][j].y;
+                    if constexpr (DM == 1) {
+                        acc = fmaf(sc, dot - xoff[j], acc);
+                        acc2 = fmaf(bi, xs[j], acc2);
+                    } else {
+                        acc += fmaf(sc, dot, bi * xs[j]);
+                    }
+                } else {
+                    acc += dot;
+                }
+            }
+            if constexpr (DM == 1) acc = __builtin_amdgcn_ldexpf(acc, nsg) + acc2;
+            tot[v] = wave_total(acc);
+        }
+        if constexpr (S == 1) {
+            if (lane == 0) epilogue(grp, tot);
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) part[slot][p][ks][v] = tot[v];
+            }
+        }
+    };
+
+    // one round in flight per wave: reduce round i, then issue round i + 1
+    int slot = 0, first = 0;
+    for (int i = 0; i < rounds; ++i) {   // uniform per block
+        finish(wbuf, pbuf, g0 + i * GP, slot);
+        const int gn = g0 + (i + 1) * GP;
+        if (gn < n_out) issue(wbuf, pbuf, gn);
+        if constexpr (S > 1) {
+            if (++slot == kBatch || i + 1 == rounds) { combine(first, slot); slot = 0; first = i + 1; }
+        }
+    }
+}
+
+// K split of the streaming kernel for rows of k codes (t 1-KiB K-tiles),
+// from measured sweeps over the Qwen3-8B, Llama-3.2-1B, Llama-3-8B 4-bit and
+// Qwen2.5-1.5B bf16 shapes: one tile per wave for t <= 3 and odd t <= 8, two
+// for other t <= 16, beyond that ceil(t/8) tiles on ceil(t/TW) waves.
+// Returns false when a wave would need more activations than registers
+// allow, or when the activation row (xb bytes per element) does not fit in
+// the LDS stage.
+struct StreamSplit { int s, tw; };
+
+bool stream_split(int bits, int k, int xb, StreamSplit& out) {
+    if (static_cast<int64_t>(k) * xb > kStreamLds) return false;
+    const int64_t rb = static_cast<int64_t>(k) * bits / 8;
+    const int t = static_cast<int>(((rb >> 4) + 63) >> 6);
+    const int tw_max = bits == 8 ? 4 : bits == 4 ? 2 : 8;
+    if (t <= 3 || (t % 2 == 1 && t <= 8)) { out = {t, 1}; return true; }
+    if (t <= 16) { out = {(t + 1) / 2, 2}; return true; }
+    const int tw = (t + 7) / 8;
+    if (tw > tw_max) return false;
+    out = {(t + tw - 1) / tw, tw};
+    return true;
+}
+
+// Row streams per block (measured): up to 12 waves per block, and at most 4
+// streams when each wave holds a single tile.  At most 12 waves keeps at
+// least 170 VGPRs per wave (three waves per SIMD), more than any split here
+// needs.
+constexpr int stream_rows_per_block(int s, int tw) {
+    const int p = s < 12 ? 12 / s : 1;
+    return tw == 1 && p > 4 ? 4 : p;
+}
+
+template <int BITS, int XDT, int ODT, bool GU, bool CHAIN, int S, int TW>
+int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s,
+                  const ChainArgs& ch) {
+    if constexpr (TW > StreamShape<BITS>::TW_MAX) {
+        return static_cast<int>(hipErrorInvalidValue);
+    } else {
+        constexpr int P = stream_rows_per_block(S, TW);
+        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, CHAIN>;
+        const size_t lds = static_cast<size_t>(k) * x_bytes<XDT>();
+        const int res = resident_blocks(kern, 64 * S * P, lds);
+        if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
+        const int need = (n_out + P - 1) / P;
+        const int blocks = need < res ? need : res;
+        return static_cast<int>(launch(kern, dim3(blocks), dim3(64 * S * P), lds, s,
+                                       static_cast<const uint8_t*>(w.q), w.scale_bias, x, r, out, n_out, k,
+                                       gshift_of(w.group), ch));
+    }
+}
+
+template <int BITS, int XDT, int ODT, bool GU, bool CHAIN, int S>
+int run_stream_s(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
+                 hipStream_t s, const ChainArgs& ch) {
+    switch (tw) {
+        case 1: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 1>(w, x, r, out, n_out, k, s, ch);
+        case 2: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 2>(w, x, r, out, n_out, k, s, ch);
+        case 3: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 3>(w, x, r, out, n_out, k, s, ch);
+        case 4: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 4>(w, x, r, out, n_out, k, s, ch);
+        case 5: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 5>(w, x, r, out, n_out, k, s, ch);
+        case 6: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 6>(w, x, r, out, n_out, k, s, ch);
+        case 7: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 7>(w, x, r, out, n_out, k, s, ch);
+        default: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 8>(w, x, r, out, n_out, k, s, ch);
+    }
+}
+
+template <int BITS, int XDT, int ODT, bool GU, bool CHAIN, int S>
+int run_stream_s12(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
+                   hipStream_t s, const ChainArgs& ch) {
+    return tw == 1 ? run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 1>(w, x, r, out, n_out, k, s, ch)
+                   : run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 2>(w, x, r, out, n_out, k, s, ch);
+}
+
+template <int BITS, int XDT, int ODT, bool GU, bool CHAIN>
+int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, const StreamSplit& sp,
+               hipStream_t s, const ChainArgs& ch) {
+    switch (sp.s) {
+        case 1: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 1>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 2: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 2>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 3: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 3>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 4: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 4>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 5: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 5>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 6: return run_stream_s<BITS, XDT, ODT, GU, CHAIN, 6>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 7: return run_stream_s<BITS, XDT, ODT, GU, CHAIN, 7>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        default: return run_stream_s<BITS, XDT, ODT, GU, CHAIN, 8>(w, x, r, out, n_out, k, sp.tw, s, ch);
+    }
+}
+
+}  // namespace
+}  // namespace qdm

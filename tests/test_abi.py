@@ -124,6 +124,36 @@ def test_mlp_rejects():
     assert f(out=ODD) == q.QDM_ERR_ALIGNMENT
 
 
+def test_chain_rejects():
+    gu = _w(n=512, k=256)
+    dn = _w(n=256, k=512)
+    A, B, NW, S, OUT, WS = (ctypes.c_void_p(0x10000 * i) for i in range(1, 7))
+    need = L.qdm_mlp_rmsnorm_workspace_bytes(1, 256, 512, q.QDM_BF16)
+    assert need == 512 * 4 + 2 * 512
+    assert L.qdm_mlp_rmsnorm_workspace_bytes(3, 256, 512, q.QDM_F32) == 3 * 512 * 4 + 2 * 3 * 256 * 4
+    assert L.qdm_mlp_rmsnorm_workspace_bytes(0, 256, 512, q.QDM_F32) == 0
+
+    def f(a=A, b=B, nw=NW, eps=1e-5, m=1, dt=q.QDM_BF16, gu=gu, dn=dn, ws=WS, wsb=need, s=S, out=OUT):
+        return L.qdm_mlp_decode_rmsnorm(a, b, nw, eps, m, dt, ctypes.byref(gu), ctypes.byref(dn), ws, wsb, s,
+                                        out, None)
+
+    assert f(wsb=need - 1) == q.QDM_ERR_WORKSPACE
+    assert f(ws=None) == q.QDM_ERR_WORKSPACE
+    assert f(m=2) == q.QDM_ERR_WORKSPACE
+    assert f(nw=None) == q.QDM_ERR_INVALID_ARG
+    assert f(out=None) == q.QDM_ERR_INVALID_ARG
+    assert f(s=OUT) == q.QDM_ERR_INVALID_ARG                          # s_out aliases out
+    assert f(ws=A, wsb=need) == q.QDM_ERR_INVALID_ARG                 # workspace aliases a
+    assert f(eps=float("nan")) == q.QDM_ERR_INVALID_ARG
+    assert f(eps=-1.0) == q.QDM_ERR_INVALID_ARG
+    assert f(dt=7) == q.QDM_ERR_INVALID_ARG
+    assert f(m=17) == q.QDM_ERR_UNSUPPORTED
+    assert f(dn=_w(n=256, k=1024)) == q.QDM_ERR_INVALID_ARG          # ffn mismatch
+    assert f(dn=_w(n=256, k=512, bits=4)) == q.QDM_ERR_UNSUPPORTED   # mixed formats
+    assert f(b=ODD) == q.QDM_ERR_ALIGNMENT
+    assert f(s=ODD) == q.QDM_ERR_ALIGNMENT
+
+
 def test_rmsnorm_rejects():
     A, B, W, S, N = (ctypes.c_void_p(0x10000 * i) for i in range(1, 6))
 

@@ -51,3 +51,16 @@ def test_rmsnorm_inputs():
     a, b, nw = W.rmsnorm_inputs(W.WORKLOADS[2])
     assert a.dtype == "f16" and a.values.shape == (1, 2048)
     assert nw.values.min() >= 0.5 and nw.values.max() <= 1.5
+
+
+def test_chain_inputs():
+    for i in (1, 2, 3, 4, 5):
+        wl = W.WORKLOADS[i]
+        a, b, nw = W.chain_inputs(wl, 2)
+        assert a.dtype == b.dtype == nw.dtype == wl.act
+        assert a.values.shape == b.values.shape == (2, wl.d) and nw.values.shape == (wl.d,)
+        assert nw.values.min() >= 0.5 and nw.values.max() <= 1.5
+        assert not np.array_equal(a.values, b.values)
+    a1, _, _ = W.chain_inputs(W.WORKLOADS[4], 1)
+    a2, _, _ = W.chain_inputs(W.WORKLOADS[4], 2)
+    assert np.array_equal(a1.values[0], a2.values[0])

@@ -14,7 +14,8 @@ sigma, activations standard normal.
 
 Seeds: every tensor is drawn from ``numpy.random.default_rng`` seeded with
 ``SeedSequence([workload_index, set_index, tensor_id])``; tensor ids are
-1 W_gate, 2 W_up, 3 W_down, 4 x, 5 r, 6 a, 7 b, 8 norm weight.
+1 W_gate, 2 W_up, 3 W_down, 4 x, 5 r, 6 a, 7 b, 8 norm weight, 9-11 the decode
+chain's a, b and norm weight.
 Activations are drawn in fp32 as one [M, d] block, so the first row of an
 M-row draw equals the 1-row draw.
 """
@@ -26,7 +27,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 TENSOR_IDS = {"w_gate": 1, "w_up": 2, "w_down": 3, "x": 4, "r": 5,
-              "a": 6, "b": 7, "norm_w": 8}
+              "a": 6, "b": 7, "norm_w": 8, "chain_a": 9, "chain_b": 10, "chain_w": 11}
 
 DTYPES = ("f32", "f16", "bf16")
 
@@ -151,6 +152,17 @@ def rmsnorm_inputs(w: Workload, rows: int = 1, set_index: int = 0):
     nw = rng_for(w.index, set_index, "norm_w").uniform(0.5, 1.5, size=w.d).astype(np.float32)
     dt = w.norm_dtype
     return to_storage(a, dt), to_storage(b, dt), to_storage(nw, dt)
+
+
+def chain_inputs(w: Workload, rows: int = 1, set_index: int = 0):
+    """(a, b, weight) for the decode chain (add + RMSNorm feeding the MLP), in
+    the MLP's activation dtype: a (the residual stream) and b (the block
+    output added to it) ~ N(0,1) [rows, d], weight ~ U(0.5, 1.5) [d] -- the
+    add+RMSNorm recipe at the MLP's shape."""
+    a = normal_f32(rng_for(w.index, set_index, "chain_a"), (rows, w.d))
+    b = normal_f32(rng_for(w.index, set_index, "chain_b"), (rows, w.d))
+    nw = rng_for(w.index, set_index, "chain_w").uniform(0.5, 1.5, size=w.d).astype(np.float32)
+    return to_storage(a, w.act), to_storage(b, w.act), to_storage(nw, w.act)
 
 
 def generic_weights(seed, n: int, k: int, sigma: float = 0.02) -> np.ndarray:
