@@ -202,6 +202,7 @@ def other_configs(samples, only=None):
         torch.cuda.empty_cache()
     if only:
         return res
+    res.update(projection_configs(samples, dev))
     # add + RMSNorm (the row-a5 kernel) on the Llama-3.2-1B-shaped f16 row, and a launch floor
     wl = W.WORKLOADS[2]
     a, b, w = W.rmsnorm_inputs(wl)
@@ -212,6 +213,59 @@ def other_configs(samples, only=None):
     z = torch.empty(1, device="cuda")
     t = graph_samples(lambda i: z.zero_(), 36, samples)
     res["launch_floor_fill_kernel"] = {"us": pcts(t)}
+    return res
+
+
+def projection_configs(samples, dev):
+    """One-row projections other than the MLP: the Qwen3-8B-shaped lm_head (vocab 151936), and
+    the four attention projections of a Qwen2.5-1.5B-shaped layer (q/k/v with bias, o without),
+    each over address-distinct weight copies of at least 2 GiB."""
+    import torch
+    import quantized_decode_mlp_amd as qdm
+    res = {}
+
+    def prepared(p):
+        w32, b, x = W.projection_inputs(p, 1)
+        q, sb = qdm.quantize_pack_rows(w32, p.bits, p.group)
+        return q, sb, (None if b is None else dev(b)), dev(x)
+
+    p = W.PROJECTIONS["qwen3_8b_lm_head"]
+    q, sb, _, xd = prepared(p)
+    copies = int(-(-(2 << 30) // p.weight_bytes))
+    ws = [qdm.Weight.from_host(p.n, p.k, p.bits, p.group, q, sb) for _ in range(copies)]
+    del q, sb
+    out = torch.empty((1, p.n), dtype=xd.dtype, device="cuda")
+    t = graph_samples(lambda i: qdm.gemv_linear(xd, ws[i], out=out), copies, samples)
+    med = float(np.median(t))
+    res["lm_head_qwen3_8b"] = {"us": pcts(t), "weight_GBps": round(p.weight_bytes / (med * 1e-6) / 1e9, 1),
+                               "hbm_frac": round(p.weight_bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                               "copies": copies}
+    _log(f"lm_head: {med:.2f} us")
+    del ws
+    torch.cuda.empty_cache()
+
+    keys = ("qwen25_1p5b_q", "qwen25_1p5b_k", "qwen25_1p5b_v", "qwen25_1p5b_o")
+    prep = [prepared(W.PROJECTIONS[k]) for k in keys]
+    layer_bytes = sum(W.PROJECTIONS[k].weight_bytes for k in keys)
+    copies = int(-(-(2 << 30) // layer_bytes))
+    layers = [[(qdm.Weight.from_host(W.PROJECTIONS[k].n, W.PROJECTIONS[k].k, W.PROJECTIONS[k].bits,
+                                     W.PROJECTIONS[k].group, q, sb), bd)
+               for k, (q, sb, bd, _) in zip(keys, prep)] for _ in range(copies)]
+    xd = prep[0][3]
+    outs = [torch.empty((1, W.PROJECTIONS[k].n), dtype=xd.dtype, device="cuda") for k in keys]
+
+    def attn(i):
+        for (wt, bd), o in zip(layers[i], outs):
+            qdm.gemv_linear(xd, wt, bias=bd, out=o)
+
+    t = graph_samples(attn, copies, samples)
+    med = float(np.median(t))
+    res["attention_qkvo_qwen25_1p5b"] = {"us_per_layer": pcts(t), "launches": 4,
+                                         "weight_GBps": round(layer_bytes / (med * 1e-6) / 1e9, 1),
+                                         "copies": copies}
+    _log(f"attention q/k/v/o: {med:.2f} us per layer")
+    del layers
+    torch.cuda.empty_cache()
     return res
 
 

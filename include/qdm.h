@@ -176,6 +176,23 @@ int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act,
 int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype act,
                            const qdm_weight* down, void* out, void* stream);
 
+/* out[m][n] = x W^T + bias, fp32 accumulation, bias added in fp32, the sum
+ * rounded once (nearest-even) to the act dtype.  The one-row decode
+ * projections other than the MLP ("MLX-LM Backend" page, the passages on
+ * vocabulary compression -- an untied lm_head, or a tied embedding table used
+ * as the linear map -- and on attention-projection compression -- q/k/v/o
+ * with their biases kept): the down projection's GEMV with the bias where the
+ * residual was.
+ *   x     device, act dtype, [m][k]
+ *   w     descriptor [n][k]: bits 8/4 with group 32/64/128, or 16 (dense
+ *         bf16); a tied embedding is the [vocab][d] table itself (n = vocab).
+ *   bias  device, act dtype, [n], shared by the m rows; NULL for none.
+ *   out   device, act dtype, [m][n]; may alias neither x nor bias.
+ * One row runs on the weight-streaming kernel; 2..16 rows on the vector
+ * kernel four rows a pass. */
+int qdm_gemv_linear(const void* x, int32_t m, qdm_dtype act, const qdm_weight* w, const void* bias, void* out,
+                    void* stream);
+
 /* The whole MLP: the two launches above on one stream, h kept in `workspace`
  * (device, >= qdm_mlp_workspace_bytes(m, ffn) bytes, 16-byte aligned).
  * gate_up->k must equal down->n (= d) and gate_up->n must equal down->k (= ffn);

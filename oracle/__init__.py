@@ -20,6 +20,9 @@ What it computes (plain definitions, numpy, float64):
 * ``mlp_decode_rmsnorm`` -- the decode chain: add + RMSNorm feeding the MLP,
   the sum as its residual ("Compute-Graph Fusion" page, GraphBuilder example
   and "Automatic Gated Epilogues").
+* ``linear`` -- y = x W^T + b, the one-row vocabulary and attention
+  projections ("MLX-LM Backend" page, the passages on vocabulary and
+  attention-projection compression).
 * ``scaled_error`` -- max|out - ref| / max|ref|, the scale-normalized error
   ("Compute-Graph Fusion" page, section "Automatic Gated Epilogues").
 
@@ -34,6 +37,7 @@ from .pack import (pack_codes, unpack_codes, pack_scale_bias, unpack_scale_bias,
 from .mlp import silu, gate_up_swiglu, down_residual, mlp_decode
 from .rmsnorm import round_to_dtype, add_rmsnorm
 from .chain import mlp_decode_rmsnorm
+from .linear import linear
 from .compare import scaled_error
 
 __all__ = [
@@ -41,5 +45,5 @@ __all__ = [
     "pack_codes", "unpack_codes", "pack_scale_bias", "unpack_scale_bias",
     "pack_gate_up", "pack_gate_up_scale_bias", "pack_dense_gate_up",
     "silu", "gate_up_swiglu", "down_residual", "mlp_decode",
-    "round_to_dtype", "add_rmsnorm", "mlp_decode_rmsnorm", "scaled_error",
+    "round_to_dtype", "add_rmsnorm", "mlp_decode_rmsnorm", "linear", "scaled_error",
 ]

@@ -32,7 +32,7 @@ EXPORTS = (
     "qdm_packed_q_bytes", "qdm_scale_bias_floats", "qdm_mlp_workspace_bytes",
     "qdm_quantize_affine", "qdm_pack_rows", "qdm_quantize_pack_rows",
     "qdm_quantize_pack_gate_up", "qdm_pack_gate_up", "qdm_pack_dense_gate_up",
-    "qdm_gemv_gate_up_swiglu", "qdm_gemv_down_residual", "qdm_mlp_decode",
+    "qdm_gemv_gate_up_swiglu", "qdm_gemv_down_residual", "qdm_gemv_linear", "qdm_mlp_decode",
     "qdm_add_rmsnorm", "qdm_mlp_rmsnorm_workspace_bytes", "qdm_mlp_decode_rmsnorm",
     "qdm_status_string", "qdm_version",
 )
@@ -71,6 +71,7 @@ def _load():
         "qdm_pack_dense_gate_up": (ctypes.c_int, [vp, vp, i32, i32, vp]),
         "qdm_gemv_gate_up_swiglu": (ctypes.c_int, [vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight), vp, vp]),
         "qdm_gemv_down_residual": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight), vp, vp]),
+        "qdm_gemv_linear": (ctypes.c_int, [vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight), vp, vp, vp]),
         "qdm_mlp_decode": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
                                           ctypes.POINTER(qdm_weight), vp, sz, vp, vp]),
         "qdm_add_rmsnorm": (ctypes.c_int, [vp, vp, vp, i32, i32, f32, ctypes.c_int, vp, vp, vp]),
@@ -293,6 +294,20 @@ def gemv_down_residual(h, r, down: Weight, out=None, stream=None):
     return out
 
 
+def gemv_linear(x, w: Weight, bias=None, out=None, stream=None):
+    """A projection: out [m, n] = x [m, k] W^T (+ bias [n]), all in x's dtype."""
+    torch = _torch()
+    m = x.shape[0] if x.dim() == 2 else 1
+    if out is None:
+        out = torch.empty((m, w.n), dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or (bias is not None and bias.dtype != x.dtype):
+        raise TypeError("bias and out must have the dtype of x")
+    _check(_lib.qdm_gemv_linear(_dev(x, "x"), m, _dt(x), ctypes.byref(w.descriptor),
+                                None if bias is None else _dev(bias, "bias"), _dev(out, "out"), _stream(stream)),
+           "qdm_gemv_linear")
+    return out
+
+
 def mlp_decode(x, r, gate_up: Weight, down: Weight, workspace=None, out=None, stream=None):
     """The MLP: out = r + W_down (silu(W_gate x) * (W_up x)), x, r, out [m, d]."""
     torch = _torch()
@@ -356,6 +371,6 @@ __all__ = [
     "Weight", "QdmError", "qdm_weight", "EXPORTS", "LIB_PATH",
     "status_string", "version", "packed_q_bytes", "scale_bias_floats", "mlp_workspace_bytes",
     "quantize_affine", "pack_rows", "quantize_pack_rows", "quantize_pack_gate_up", "pack_gate_up",
-    "pack_dense_gate_up", "gemv_gate_up_swiglu", "gemv_down_residual", "mlp_decode", "add_rmsnorm",
+    "pack_dense_gate_up", "gemv_gate_up_swiglu", "gemv_down_residual", "gemv_linear", "mlp_decode", "add_rmsnorm",
     "mlp_rmsnorm_workspace_bytes", "mlp_decode_rmsnorm",
 ]

@@ -72,6 +72,17 @@ int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype a
     return hip_status(qdm::launch_down_residual(h, r, m, act, *down, out, stream));
 }
 
+int qdm_gemv_linear(const void* x, int32_t m, qdm_dtype act, const qdm_weight* w, const void* bias, void* out,
+                    void* stream) {
+    if (!x || !out) return QDM_ERR_INVALID_ARG;
+    if (x == out || (bias && bias == out)) return QDM_ERR_INVALID_ARG;
+    if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
+    if (int e = check_rows(m)) return e;
+    if (int e = check_weight(w)) return e;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(bias, 16)) return QDM_ERR_ALIGNMENT;
+    return hip_status(qdm::launch_linear(x, m, act, *w, bias, out, stream));
+}
+
 int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
                    const qdm_weight* gate_up, const qdm_weight* down,
                    void* workspace, size_t workspace_bytes, void* out, void* stream) {

@@ -49,12 +49,14 @@ __device__ __forceinline__ void dot_dword(uint32_t w, const float (&xv)[M][EPD],
 }
 
 // GU: gate/up pairs (q rows interleaved [n][2][k]), epilogue h = silu(g) * u (fp32 out).
-// !GU: single rows, epilogue out = r + acc rounded to ODT.
+// !GU: single rows, epilogue out = r + acc rounded to ODT, r's rows r_row
+// elements apart (0: one row shared by all, e.g. a projection's bias); no r
+// when resid is null.
 template <int BITS, int XDT, int ODT, int M, bool GU>
 __global__ void __launch_bounds__(64 * kWaves)
 qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
              const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
-             int n_out, int k, int gshift, int m_rows) {
+             int n_out, int k, int gshift, int m_rows, int r_row) {
     constexpr int E = 128 / BITS;   // codes per 16-byte chunk
     constexpr int EPD = E / 4;      // codes per dword
     constexpr int NV = GU ? 2 : 1;
@@ -179,7 +181,8 @@ qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                 const float sg = a0 / (1.0f + expf(-a0));
                 static_cast<float*>(out)[o] = sg * a1;
             } else {
-                store_elem<ODT>(out, o, load_elem<ODT>(resid, o) + a0);
+                const int64_t ro = static_cast<int64_t>(m) * r_row + row0 + r;
+                store_elem<ODT>(out, o, resid ? load_elem<ODT>(resid, ro) + a0 : a0);
             }
         }
     }
@@ -188,20 +191,21 @@ qgemv_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 
 template <int BITS, int XDT, int ODT, int M, bool GU>
 int run(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int m_rows,
-        hipStream_t s) {
+        hipStream_t s, int r_row) {
     dim3 grid((n_out + kRows - 1) / kRows), block(64 * kWaves);
     return static_cast<int>(launch(qgemv_kernel<BITS, XDT, ODT, M, GU>, grid, block, 0, s,
                                    static_cast<const uint8_t*>(w.q), w.scale_bias, x, r, out, n_out, k,
-                                   gshift_of(w.group), m_rows));
+                                   gshift_of(w.group), m_rows, r_row));
 }
 
+// r_row: elements between r's rows (the output's row length for a residual)
 template <int XDT, int ODT, int M, bool GU>
 int run_bits(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k,
-             int m_rows, hipStream_t s) {
+             int m_rows, hipStream_t s, int r_row) {
     switch (w.bits) {
-        case 8: return run<8, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s);
-        case 4: return run<4, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s);
-        default: return run<16, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s);
+        case 8: return run<8, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s, r_row);
+        case 4: return run<4, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s, r_row);
+        default: return run<16, XDT, ODT, M, GU>(w, x, r, out, n_out, k, m_rows, s, r_row);
     }
 }
 
@@ -214,12 +218,12 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
         StreamSplit sp;
         if (stream_split(w.bits, k, x_bytes<XDT>(), sp)) {
             switch (w.bits) {
-                case 8: return run_stream<8, XDT, ODT, GU, false>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
-                case 4: return run_stream<4, XDT, ODT, GU, false>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
-                default: return run_stream<16, XDT, ODT, GU, false>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
+                case 8: return run_stream<8, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
+                case 4: return run_stream<4, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
+                default: return run_stream<16, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
             }
         }
-        return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s);
+        return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s, n_out);
     }
     // 2..16 rows on the matrix cores.  Gate/up with 8/4-bit weights and 16-bit
     // activations, down with 8/4-bit weights and a 16-bit output: the
@@ -248,13 +252,47 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
         const void* xp = static_cast<const char*>(x) + static_cast<size_t>(m0) * x_row * xe;
         const void* rp = r ? static_cast<const char*>(r) + static_cast<size_t>(m0) * o_row * oe : nullptr;
         void* op = static_cast<char*>(out) + static_cast<size_t>(m0) * o_row * oe;
-        const int e = run_bits<XDT, ODT, 4, GU>(w, xp, rp, op, n_out, k, mr, s);
+        const int e = run_bits<XDT, ODT, 4, GU>(w, xp, rp, op, n_out, k, mr, s, static_cast<int>(o_row));
+        if (e) return e;
+    }
+    return 0;
+}
+
+// A projection out[m][n] = x W^T (+ bias): one row on the streaming kernel,
+// several on the vector kernel four rows a pass, the bias shared by the rows.
+template <int XDT>
+int run_linear(const qdm_weight& w, const void* x, int m, const void* bias, void* out, hipStream_t s) {
+    const int n = w.n, k = w.k;
+    StreamSplit sp;
+    if (m == 1 && stream_split(w.bits, k, x_bytes<XDT>(), sp)) {
+        switch (w.bits) {
+            case 8: return run_stream<8, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
+            case 4: return run_stream<4, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
+            default: return run_stream<16, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
+        }
+    }
+    const size_t xe = XDT == DT_F32 ? 4 : 2;
+    for (int m0 = 0; m0 < m; m0 += 4) {
+        const int mr = m - m0 < 4 ? m - m0 : 4;
+        const void* xp = static_cast<const char*>(x) + static_cast<size_t>(m0) * k * xe;
+        void* op = static_cast<char*>(out) + static_cast<size_t>(m0) * n * xe;
+        const int e = mr == 1 ? run_bits<XDT, XDT, 1, false>(w, xp, bias, op, n, k, 1, s, 0)
+                              : run_bits<XDT, XDT, 4, false>(w, xp, bias, op, n, k, mr, s, 0);
         if (e) return e;
     }
     return 0;
 }
 
 }  // namespace
+
+int launch_linear(const void* x, int m, int act, const qdm_weight& w, const void* bias, void* out, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (act) {
+        case DT_F32: return run_linear<DT_F32>(w, x, m, bias, out, s);
+        case DT_F16: return run_linear<DT_F16>(w, x, m, bias, out, s);
+        default: return run_linear<DT_BF16>(w, x, m, bias, out, s);
+    }
+}
 
 int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -13,6 +13,8 @@ int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, f
                           void* stream);
 int launch_down_residual(const float* h, const void* r, int m, int act, const qdm_weight& dn,
                          void* out, void* stream);
+// A projection out[m][n] = x W^T (+ bias[n] when bias is not null), act dtype in and out.
+int launch_linear(const void* x, int m, int act, const qdm_weight& w, const void* bias, void* out, void* stream);
 // Few-row (2..16) projections on the matrix cores (qdm_mfma.hip).
 bool mma_rows_supported(const qdm_weight& w, int m);
 int launch_gate_up_mma(const void* x_bf16, int m, const qdm_weight& gu, float* h, void* stream);

@@ -1,8 +1,10 @@
 // One-row streaming GEMV kernel for gfx950 (gate/up with the SwiGLU epilogue,
 // down with the residual epilogue) and its host launchers, optionally with
-// the decode chain's residual add + RMSNorm folded in (CHAIN).  Included by
-// qdm_gemv.hip (plain projections) and qdm_chain.hip (the chained forms);
-// each translation unit instantiates what it launches.
+// the decode chain's residual add + RMSNorm folded in, or as a plain
+// projection with an optional bias (the epilogue mode EPI).  Included by
+// qdm_gemv.hip (the MLP's projections and the plain projection) and
+// qdm_chain.hip (the chained forms); each translation unit instantiates what
+// it launches.
 //
 // Pages: meTile docs, "Compute-Graph Fusion", section "Automatic Gated
 // Epilogues" (two projections sharing the activation, silu(gate) * up on chip,
@@ -21,6 +23,13 @@
 #include "qdm_launch.h"
 
 namespace qdm {
+
+// Epilogue modes of the streaming kernel.  Plain: SwiGLU (gate/up) or the
+// residual add (down).  Chain: the decode chain's forms.  Linear (down only):
+// a projection, out = acc (+ bias[row] when the residual pointer is not null).
+constexpr int kEpiPlain = 0;
+constexpr int kEpiChain = 1;
+constexpr int kEpiLinear = 2;
 
 // Inputs of the chained forms (unused otherwise).  Gate/up: the block's
 // activation row is n = rmsnorm(a + b) * w, recomputed in every block.  Down:
@@ -99,7 +108,7 @@ __device__ __forceinline__ uint32_t dword_map(uint32_t xa, uint32_t xb, F f) {
     }
 }
 
-template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P, bool CHAIN>
+template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P, int EPI>
 __global__ void __launch_bounds__(64 * S * P)
 qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                     const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
@@ -110,7 +119,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     constexpr bool AFFINE = BITS != 16;
     constexpr int NT = 64 * S * P;
     constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
-    constexpr bool NORM = CHAIN && GU;   // the activation row is rmsnorm(a + b) * w
+    constexpr bool NORM = EPI == kEpiChain && GU;   // the activation row is rmsnorm(a + b) * w
     constexpr int kNormThreads = 256;    // the standalone add + RMSNorm kernel's block
     static_assert(!NORM || NT >= kNormThreads, "the norm prologue needs four waves");
 
@@ -327,11 +336,14 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         if constexpr (GU) {
             const float gs = t[0];
             static_cast<float*>(out)[grp] = gs / (1.0f + expf(-gs)) * t[NV - 1];
-        } else if constexpr (CHAIN) {
+        } else if constexpr (EPI == kEpiChain) {
             // the residual is the chain's sum s = a + b, rounded once as stored
             const float sv = round_trip<ODT>(load_elem<ODT>(ch.a, grp) + load_elem<ODT>(ch.b, grp));
             if (ch.s_out) store_elem<ODT>(ch.s_out, grp, sv);
             store_elem<ODT>(out, grp, sv + t[0]);
+        } else if constexpr (EPI == kEpiLinear) {
+            // a projection: the optional bias takes the residual's place
+            store_elem<ODT>(out, grp, resid ? load_elem<ODT>(resid, grp) + t[0] : t[0]);
         } else {
             store_elem<ODT>(out, grp, load_elem<ODT>(resid, grp) + t[0]);
         }
@@ -469,14 +481,14 @@ constexpr int stream_rows_per_block(int s, int tw) {
     return tw == 1 && p > 4 ? 4 : p;
 }
 
-template <int BITS, int XDT, int ODT, bool GU, bool CHAIN, int S, int TW>
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int S, int TW>
 int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s,
                   const ChainArgs& ch) {
     if constexpr (TW > StreamShape<BITS>::TW_MAX) {
         return static_cast<int>(hipErrorInvalidValue);
     } else {
         constexpr int P = stream_rows_per_block(S, TW);
-        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, CHAIN>;
+        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, EPI>;
         const size_t lds = static_cast<size_t>(k) * x_bytes<XDT>();
         const int res = resident_blocks(kern, 64 * S * P, lds);
         if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
@@ -488,40 +500,40 @@ int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, 
     }
 }
 
-template <int BITS, int XDT, int ODT, bool GU, bool CHAIN, int S>
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int S>
 int run_stream_s(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
                  hipStream_t s, const ChainArgs& ch) {
     switch (tw) {
-        case 1: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 1>(w, x, r, out, n_out, k, s, ch);
-        case 2: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 2>(w, x, r, out, n_out, k, s, ch);
-        case 3: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 3>(w, x, r, out, n_out, k, s, ch);
-        case 4: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 4>(w, x, r, out, n_out, k, s, ch);
-        case 5: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 5>(w, x, r, out, n_out, k, s, ch);
-        case 6: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 6>(w, x, r, out, n_out, k, s, ch);
-        case 7: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 7>(w, x, r, out, n_out, k, s, ch);
-        default: return run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 8>(w, x, r, out, n_out, k, s, ch);
+        case 1: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 1>(w, x, r, out, n_out, k, s, ch);
+        case 2: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 2>(w, x, r, out, n_out, k, s, ch);
+        case 3: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 3>(w, x, r, out, n_out, k, s, ch);
+        case 4: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 4>(w, x, r, out, n_out, k, s, ch);
+        case 5: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 5>(w, x, r, out, n_out, k, s, ch);
+        case 6: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 6>(w, x, r, out, n_out, k, s, ch);
+        case 7: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 7>(w, x, r, out, n_out, k, s, ch);
+        default: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 8>(w, x, r, out, n_out, k, s, ch);
     }
 }
 
-template <int BITS, int XDT, int ODT, bool GU, bool CHAIN, int S>
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int S>
 int run_stream_s12(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
                    hipStream_t s, const ChainArgs& ch) {
-    return tw == 1 ? run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 1>(w, x, r, out, n_out, k, s, ch)
-                   : run_stream_st<BITS, XDT, ODT, GU, CHAIN, S, 2>(w, x, r, out, n_out, k, s, ch);
+    return tw == 1 ? run_stream_st<BITS, XDT, ODT, GU, EPI, S, 1>(w, x, r, out, n_out, k, s, ch)
+                   : run_stream_st<BITS, XDT, ODT, GU, EPI, S, 2>(w, x, r, out, n_out, k, s, ch);
 }
 
-template <int BITS, int XDT, int ODT, bool GU, bool CHAIN>
+template <int BITS, int XDT, int ODT, bool GU, int EPI>
 int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, const StreamSplit& sp,
                hipStream_t s, const ChainArgs& ch) {
     switch (sp.s) {
-        case 1: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 1>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 2: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 2>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 3: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 3>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 4: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 4>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 5: return run_stream_s12<BITS, XDT, ODT, GU, CHAIN, 5>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 6: return run_stream_s<BITS, XDT, ODT, GU, CHAIN, 6>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 7: return run_stream_s<BITS, XDT, ODT, GU, CHAIN, 7>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        default: return run_stream_s<BITS, XDT, ODT, GU, CHAIN, 8>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 1: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 1>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 2: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 2>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 3: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 3>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 4: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 4>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 5: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 5>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 6: return run_stream_s<BITS, XDT, ODT, GU, EPI, 6>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 7: return run_stream_s<BITS, XDT, ODT, GU, EPI, 7>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        default: return run_stream_s<BITS, XDT, ODT, GU, EPI, 8>(w, x, r, out, n_out, k, sp.tw, s, ch);
     }
 }
 

@@ -124,6 +124,26 @@ def test_mlp_rejects():
     assert f(out=ODD) == q.QDM_ERR_ALIGNMENT
 
 
+def test_linear_rejects():
+    X, BIAS, OUT = (ctypes.c_void_p(0x10000 * i) for i in range(1, 4))
+
+    def f(x=X, m=1, dt=q.QDM_BF16, w=None, bias=BIAS, out=OUT):
+        w = _w(n=300, k=256) if w is None else w
+        return L.qdm_gemv_linear(x, m, dt, ctypes.byref(w), bias, out, None)
+
+    assert f(x=None) == q.QDM_ERR_INVALID_ARG
+    assert f(out=None) == q.QDM_ERR_INVALID_ARG
+    assert f(out=X) == q.QDM_ERR_INVALID_ARG                          # out aliases x
+    assert f(out=BIAS) == q.QDM_ERR_INVALID_ARG                       # out aliases bias
+    assert f(m=0) == q.QDM_ERR_INVALID_ARG
+    assert f(m=17) == q.QDM_ERR_UNSUPPORTED
+    assert f(dt=5) == q.QDM_ERR_INVALID_ARG
+    assert f(w=_w(n=300, k=256, bits=2)) == q.QDM_ERR_UNSUPPORTED
+    assert f(w=_w(n=300, k=250, group=32)) == q.QDM_ERR_INVALID_ARG
+    assert f(bias=ODD) == q.QDM_ERR_ALIGNMENT
+    assert f(x=ODD) == q.QDM_ERR_ALIGNMENT
+
+
 def test_chain_rejects():
     gu = _w(n=512, k=256)
     dn = _w(n=256, k=512)

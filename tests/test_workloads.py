@@ -64,3 +64,15 @@ def test_chain_inputs():
     a1, _, _ = W.chain_inputs(W.WORKLOADS[4], 1)
     a2, _, _ = W.chain_inputs(W.WORKLOADS[4], 2)
     assert np.array_equal(a1.values[0], a2.values[0])
+
+
+def test_projection_inputs():
+    for key, p in W.PROJECTIONS.items():
+        if p.n * p.k > 10_000_000:
+            continue
+        w, b, x = W.projection_inputs(p, 3)
+        assert w.shape == (p.n, p.k) and x.values.shape == (3, p.k) and x.dtype == p.act
+        assert (b is not None) == p.bias
+        w2, _, _ = W.projection_inputs(p, 1)
+        assert np.array_equal(w, w2)
+    assert W.PROJECTIONS["qwen3_8b_lm_head"].weight_bytes == 151936 * 4096 + 8 * 151936 * 4096 // 128

@@ -72,6 +72,57 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class Projection:
+    """A one-row decode projection other than the MLP (vocabulary or attention)."""
+    key: str
+    name: str
+    n: int                # output rows (vocabulary size, or the projection's width)
+    k: int                # input dim
+    bits: int
+    group: int
+    act: str
+    sigma: float          # weight standard deviation
+    bias: bool            # the projection keeps a bias
+    seed_id: int
+
+    @property
+    def weight_bytes(self) -> int:
+        if self.bits == 16:
+            return 2 * self.n * self.k
+        return self.n * self.k * self.bits // 8 + 8 * (self.n * self.k // self.group)
+
+
+# Vocabulary projections at the shapes of the pages' Qwen 3 8B (untied
+# lm_head) and Llama 3.2 1B (tied embedding used as the output map), and the
+# attention projections of a Qwen 2.5 1.5B-shaped layer (q/k/v with biases, o
+# without; 12 query and 2 key/value heads of 128) at affine group 32.
+PROJECTIONS = {p.key: p for p in (
+    Projection("qwen3_8b_lm_head", "Qwen3-8B-shaped untied lm_head: vocab 151936 x d 4096, uint8 g128",
+               151936, 4096, 8, 128, "bf16", 0.02, False, 101),
+    Projection("llama32_1b_tied_embedding", "Llama-3.2-1B-shaped tied embedding as output map: vocab 128256 "
+               "x d 2048, uint8 g64", 128256, 2048, 8, 64, "bf16", 0.02, False, 102),
+    Projection("qwen25_1p5b_q", "Qwen2.5-1.5B-shaped q_proj 1536 x 1536 + bias, uint8 g32",
+               1536, 1536, 8, 32, "bf16", 0.02, True, 103),
+    Projection("qwen25_1p5b_k", "Qwen2.5-1.5B-shaped k_proj 256 x 1536 + bias, uint8 g32",
+               256, 1536, 8, 32, "bf16", 0.02, True, 104),
+    Projection("qwen25_1p5b_v", "Qwen2.5-1.5B-shaped v_proj 256 x 1536 + bias, uint8 g32",
+               256, 1536, 8, 32, "bf16", 0.02, True, 105),
+    Projection("qwen25_1p5b_o", "Qwen2.5-1.5B-shaped o_proj 1536 x 1536, uint8 g32",
+               1536, 1536, 8, 32, "bf16", 0.02, False, 106),
+)}
+
+
+def projection_inputs(p: Projection, m: int = 1, copy: int = 0):
+    """(W fp32 [n, k] ~ N(0, sigma), bias Act [n] ~ N(0, 0.1) or None, x Act [m, k] ~ N(0, 1))."""
+    def rng(t):
+        return np.random.default_rng(np.random.SeedSequence([p.seed_id, copy, t]))
+    w = normal_f32(rng(1), (p.n, p.k), p.sigma)
+    b = to_storage(normal_f32(rng(2), (p.n,), 0.1), p.act) if p.bias else None
+    x = to_storage(normal_f32(rng(3), (m, p.k)), p.act)
+    return w, b, x
+
+
 def rng_for(workload: int, set_index: int, tensor: str) -> np.random.Generator:
     seq = np.random.SeedSequence([int(workload), int(set_index), TENSOR_IDS[tensor]])
     return np.random.default_rng(seq)
