@@ -203,6 +203,7 @@ def other_configs(samples, only=None):
     if only:
         return res
     res.update(projection_configs(samples, dev))
+    res["group_sweep"] = group_sweep(samples, dev)
     # add + RMSNorm (the row-a5 kernel) on the Llama-3.2-1B-shaped f16 row, and a launch floor
     wl = W.WORKLOADS[2]
     a, b, w = W.rmsnorm_inputs(wl)
@@ -213,6 +214,42 @@ def other_configs(samples, only=None):
     z = torch.empty(1, device="cuda")
     t = graph_samples(lambda i: z.zero_(), 36, samples)
     res["launch_floor_fill_kernel"] = {"us": pcts(t)}
+    return res
+
+
+def group_sweep(samples, dev):
+    """The one-row MLP of each quantized workload shape at affine groups 32, 64 and 128 (the
+    groups the pages race per shape), over address-distinct copies of at least 2 GiB."""
+    import torch
+    import quantized_decode_mlp_amd as qdm
+    res = {}
+    for wi in (2, 4, 5):
+        wl = W.WORKLOADS[wi]
+        g32, u32, d32 = W.weights_f32(wl, 0)
+        x, r = W.activations(wl, 1)
+        xd, rd = dev(x), dev(r)
+        ws = torch.empty(qdm.mlp_workspace_bytes(1, wl.ffn), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(rd)
+        row = {}
+        for group in (32, 64, 128):
+            q, sb = qdm.quantize_pack_gate_up(g32, u32, wl.bits, group)
+            dq, dsb = qdm.quantize_pack_rows(d32, wl.bits, group)
+            n_w = 3 * wl.d * wl.ffn
+            nbytes = n_w * wl.bits // 8 + 8 * (n_w // group)
+            copies = int(-(-(2 << 30) // nbytes))
+            sets = [(qdm.Weight.from_host(wl.ffn, wl.d, wl.bits, group, q, sb),
+                     qdm.Weight.from_host(wl.d, wl.ffn, wl.bits, group, dq, dsb)) for _ in range(copies)]
+            del q, sb, dq, dsb
+            t = graph_samples(lambda i: qdm.mlp_decode(xd, rd, *sets[i], workspace=ws, out=out), copies, samples)
+            med = float(np.median(t))
+            row[f"g{group}"] = {"us_per_layer": round(med, 3), "weight_bytes": nbytes,
+                                "weight_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+            _log(f"group sweep workload {wi} g{group}: {med:.2f} us/layer")
+            del sets
+            torch.cuda.empty_cache()
+        res[f"workload{wi}_m1"] = row
+        del g32, u32, d32
     return res
 
 

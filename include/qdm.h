@@ -224,7 +224,10 @@ size_t qdm_mlp_rmsnorm_workspace_bytes(int32_t m, int32_t d, int32_t ffn, qdm_dt
  * with x = n and r = s.  With one row and shapes the one-row streaming
  * kernels take, two launches: every gate/up block recomputes s, the mean
  * square and n from a, b and w, and the down launch adds s as its residual
- * (n and s never go to HBM).  Otherwise the three launches run in order
+ * (n and s never go to HBM).  With 2..16 rows on the matrix-core kernels
+ * every gate/up block rebuilds n likewise and s goes through the workspace
+ * to the down projection (which then uses the device scratch described at
+ * qdm_gemv_down_residual).  Otherwise the three launches run in order
  * through the workspace.
  *   a, b     device, act dtype, [m][d]; out may alias either.
  *   norm_w   device, act dtype, [d];  eps >= 0 and finite.

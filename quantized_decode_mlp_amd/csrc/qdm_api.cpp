@@ -130,11 +130,21 @@ int qdm_mlp_decode_rmsnorm(const void* a, const void* b, const void* norm_w, flo
     if (m == 1 && qdm::chain_stream_supported(*gate_up, *down, act))
         return hip_status(qdm::launch_mlp_chain_stream(a, b, norm_w, eps, act, *gate_up, *down, h, s_out, out,
                                                        stream));
-    // otherwise the three launches: add + RMSNorm into the workspace (s into
-    // s_out when given), then the MLP on n with s as the residual
     char* base = static_cast<char*>(workspace);
     const size_t hb = round256(static_cast<size_t>(m) * static_cast<size_t>(ffn) * sizeof(float));
     const size_t vb = round256(static_cast<size_t>(m) * static_cast<size_t>(d) * act_bytes(act));
+    // 2..16 rows on the matrix-core kernels: the norm rebuilt in every gate/up
+    // block, s through the workspace to the down projection's residual (and to
+    // s_out by its last kernel)
+    if (m > 1 && qdm::mma_stream_gate_up_supported(*gate_up, m, act) &&
+        qdm::mma_stream_down_supported(*down, m, act)) {
+        void* s_ws = base + hb + vb;
+        if (int e = qdm::launch_gate_up_mma_stream_norm(a, b, norm_w, eps, m, act, *gate_up, h, s_ws, stream))
+            return hip_status(e);
+        return hip_status(qdm::launch_down_mma_stream(h, s_ws, m, act, *down, out, stream, s_out));
+    }
+    // otherwise the three launches: add + RMSNorm into the workspace (s into
+    // s_out when given), then the MLP on n with s as the residual
     void* n_buf = base + hb;
     void* s_buf = s_out ? s_out : static_cast<void*>(base + hb + vb);
     if (int e = qdm::launch_add_rmsnorm(a, b, norm_w, m, d, eps, act, s_buf, n_buf, stream)) return hip_status(e);

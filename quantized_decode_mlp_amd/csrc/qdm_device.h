@@ -59,6 +59,22 @@ __device__ __forceinline__ float round_trip(float v) {
     else return f16_to_f32(f32_to_f16(v));
 }
 
+// Element-wise f over the activation-type values packed in two dwords (one
+// fp32 value, or two 16-bit values low half first); the results are rounded
+// once to the type and packed the same way.
+template <int DT, typename F>
+__device__ __forceinline__ uint32_t dword_map(uint32_t xa, uint32_t xb, F f) {
+    if constexpr (DT == DT_F32) {
+        return __float_as_uint(f(__uint_as_float(xa), __uint_as_float(xb)));
+    } else {
+        auto val = [](uint32_t h) { return DT == DT_BF16 ? bf16_to_f32(h) : f16_to_f32(h); };
+        auto bits = [](float v) -> uint32_t { return DT == DT_BF16 ? f32_to_bf16(v) : f32_to_f16(v); };
+        const uint32_t lo = bits(f(val(xa & 0xffffu), val(xb & 0xffffu)));
+        const uint32_t hi = bits(f(val(xa >> 16), val(xb >> 16)));
+        return lo | (hi << 16);
+    }
+}
+
 // Loads N consecutive elements (N * sizeof(elem) in {4, 8, 16, 32} bytes, aligned
 // to min(16, that size)) as fp32.
 template <int DT, int N>

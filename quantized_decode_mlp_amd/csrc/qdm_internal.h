@@ -23,12 +23,17 @@ int launch_down_mma(const float* h, const void* r, int m, int act, const qdm_wei
 // streaming the weights once (qdm_mma_stream.hip).
 bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act);
 int launch_gate_up_mma_stream(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream);
+// The same with the decode chain's rows: x = rmsnorm(a + b) * w per row, recomputed
+// in every block; block 0 stores s = a + b to s_buf (act dtype, [m][k]).
+int launch_gate_up_mma_stream_norm(const void* a, const void* b, const void* w, float eps, int m, int act,
+                                   const qdm_weight& gu, float* h, void* s_buf, void* stream);
 // 2..16 rows, 8/4-bit affine weights, 16-bit output: K split across blocks
 // with the partials in a device scratch the library allocates on first use
 // (qdm_mma_down.hip).
 bool mma_stream_down_supported(const qdm_weight& w, int m, int act);
+// r_copy: when not null, also receives r (the decode chain's s).
 int launch_down_mma_stream(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
-                           void* stream);
+                           void* stream, void* r_copy = nullptr);
 // One row, both projections on the streaming kernels: the decode chain with
 // add + RMSNorm folded into the MLP's two launches (qdm_chain.hip).
 bool chain_stream_supported(const qdm_weight& gu, const qdm_weight& dn, int act);

@@ -254,7 +254,7 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
 template <int ODT>
 __global__ void __launch_bounds__(256)
 qmm_down_reduce_kernel(const float* __restrict__ part, const void* __restrict__ r, void* __restrict__ out, int N,
-                       int m_rows, int NS) {
+                       int m_rows, int NS, void* __restrict__ r_copy) {
     const int idx = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
     if (idx >= m_rows * N) return;
     const size_t stride = static_cast<size_t>(m_rows) * N;
@@ -269,6 +269,7 @@ qmm_down_reduce_kernel(const float* __restrict__ part, const void* __restrict__ 
         for (int j = 0; j < 8; ++j) acc += v[j];
     }
     store_elem<ODT>(out, idx, rv + acc);
+    if (r_copy) store_elem<ODT>(r_copy, idx, rv);   // the residual's copy, when asked (the decode chain's s)
 }
 
 // Slice length KR and tile groups per slice TB.  A wave's range (KR / S) is
@@ -336,7 +337,7 @@ float* down_scratch(size_t bytes, hipStream_t s, int& err) {
 }
 
 template <int BITS, int G, int ODT>
-int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s) {
+int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* r_copy) {
     constexpr int NT = 64 * kDS * kDP;
     constexpr int U = BlockLayout<BITS, G>::KBK == 128 ? kDU / 2 : kDU;
     int dev = 0, cus = 0;
@@ -358,22 +359,22 @@ int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int 
     if (e != hipSuccess) return static_cast<int>(e);
     const int outs = m * w.n;
     e = launch(qmm_down_reduce_kernel<ODT>, dim3((outs + 255) / 256), dim3(256), 0, s,
-               static_cast<const float*>(part), r, out, w.n, m, ns);
+               static_cast<const float*>(part), r, out, w.n, m, ns, r_copy);
     return static_cast<int>(e);
 }
 
 template <int BITS, int ODT>
-int run_down_g(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s) {
+int run_down_g(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* rc) {
     switch (w.group) {
-        case 32: return run_down<BITS, 32, ODT>(w, h, r, out, m, s);
-        case 64: return run_down<BITS, 64, ODT>(w, h, r, out, m, s);
-        default: return run_down<BITS, 128, ODT>(w, h, r, out, m, s);
+        case 32: return run_down<BITS, 32, ODT>(w, h, r, out, m, s, rc);
+        case 64: return run_down<BITS, 64, ODT>(w, h, r, out, m, s, rc);
+        default: return run_down<BITS, 128, ODT>(w, h, r, out, m, s, rc);
     }
 }
 
 template <int ODT>
-int run_down_b(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s) {
-    return w.bits == 8 ? run_down_g<8, ODT>(w, h, r, out, m, s) : run_down_g<4, ODT>(w, h, r, out, m, s);
+int run_down_b(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* rc) {
+    return w.bits == 8 ? run_down_g<8, ODT>(w, h, r, out, m, s, rc) : run_down_g<4, ODT>(w, h, r, out, m, s, rc);
 }
 
 template <int BITS, int G>
@@ -398,9 +399,10 @@ bool mma_stream_down_supported(const qdm_weight& w, int m, int act) {
 }
 
 int launch_down_mma_stream(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
-                           void* stream) {
+                           void* stream, void* r_copy) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return act == DT_F16 ? run_down_b<DT_F16>(dn, h, r, out, m, s) : run_down_b<DT_BF16>(dn, h, r, out, m, s);
+    return act == DT_F16 ? run_down_b<DT_F16>(dn, h, r, out, m, s, r_copy)
+                         : run_down_b<DT_BF16>(dn, h, r, out, m, s, r_copy);
 }
 
 }  // namespace qdm

@@ -50,19 +50,31 @@ size_t gate_up_lds_bytes(int m, int k) {
            static_cast<size_t>(k / BlockLayout<BITS, G>::FG) * kRows * 4;
 }
 
-template <int BITS, int XDT, int G, int S, int P, int U, int XPT, int NPL>
+// Inputs of the decode-chain form (NORM): the staged rows are
+// n = rmsnorm(a + b) * w with a = xin, and block 0 stores s = a + b to s_buf.
+struct NormArgs {
+    const void* b;
+    const void* w;
+    void* s_buf;
+    float eps;
+};
+
+template <int BITS, int XDT, int G, int S, int P, int U, int XPT, int NPL, bool NORM>
 __global__ void __launch_bounds__(64 * S * P)
 qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, const void* __restrict__ xin,
-                          float* __restrict__ hout, int N, int K, int m_rows) {
+                          float* __restrict__ hout, int N, int K, int m_rows, NormArgs na) {
     using SC = StepCodes<BITS, XDT>;
     using L = BlockLayout<BITS, G>;
     constexpr int NT = 64 * S * P;
     constexpr int KBK = L::KBK, STEPS = L::STEPS, NF = L::NF, FG = L::FG;
     constexpr bool WIDE = L::WIDE;
     constexpr int CPF = FG / 8;   // 16-byte activation pieces per fold chunk
+    constexpr int kNormThreads = 256;   // the standalone add + RMSNorm kernel's block
+    static_assert(!NORM || NT % kNormThreads == 0, "the norm prologue takes rows in 256-thread groups");
 
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ f32x4 part[S > 1 ? S - 1 : 1][P][2][64];
+    __shared__ float nred[NORM ? kRows : 1][kNormThreads / 64];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -87,11 +99,15 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
     const int ppr = K / 8;
     const int npieces = m_rows * ppr;
     const u32x4* xg = static_cast<const u32x4*>(xin);
-    u32x4 xt[XPT];
+    const u32x4* bg = static_cast<const u32x4*>(na.b);
+    u32x4 xt[XPT], bt[XPT];
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
         const int u = static_cast<int>(threadIdx.x) + j * NT;
-        if (u < npieces) xt[j] = xg[u];
+        if (u < npieces) {
+            xt[j] = xg[u];
+            if constexpr (NORM) bt[j] = bg[u];
+        }
     }
 
     using Words = typename L::Words;
@@ -189,11 +205,71 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
         if (u < npieces && c % CPF == 0) xsum[(c / CPF) * kRows + m] = sum;
     };
+    if constexpr (NORM) {
+        // The decode chain's RMSNorm per row, recomputed by every block: s =
+        // a + b rounded once, staged as is (block 0 also stores it for the
+        // down projection's residual); each row's mean square summed exactly
+        // as the standalone add + RMSNorm kernel sums it (its 256 threads'
+        // strided sums, wave sums, the four in order; rows in 256-thread
+        // groups); then n = s * inv * w rounded once goes through stage_piece
+        // in place.  n is the value that kernel would store.
+        const int tid = static_cast<int>(threadIdx.x);
+        u32x4* sg = static_cast<u32x4*>(na.s_buf);
+        auto sum_piece = [&](int u, const u32x4 av, const u32x4 bv) {
+            const int m = u / ppr, c = u - m * ppr;
+            u32x4 sv;
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) stage_piece(static_cast<int>(threadIdx.x) + j * NT, xt[j]);
-    for (int u0 = XPT * NT; u0 < npieces; u0 += NT) {
-        const int u = u0 + static_cast<int>(threadIdx.x);
-        stage_piece(u, u < npieces ? xg[u] : u32x4{0u, 0u, 0u, 0u});
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t aw = av[i], bw = bv[i];
+                sv[i] = dword_map<XDT>(aw, bw, [](float x, float y) { return x + y; });
+            }
+            *reinterpret_cast<u32x4*>(xs + m * ldx + c * 8) = sv;
+            if (blockIdx.x == 0) sg[u] = sv;
+        };
+#pragma unroll
+        for (int j = 0; j < XPT; ++j)
+            if (tid + j * NT < npieces) sum_piece(tid + j * NT, xt[j], bt[j]);
+        for (int u = XPT * NT + tid; u < npieces; u += NT) sum_piece(u, xg[u], bg[u]);
+        __syncthreads();
+        const int t = tid & (kNormThreads - 1);
+        for (int m = tid / kNormThreads; m < m_rows; m += NT / kNormThreads) {
+            float ss = 0.f;
+            for (int i = t; i < K; i += kNormThreads) {
+                const uint32_t e = xs[m * ldx + i];
+                const float v = XDT == DT_BF16 ? bf16_to_f32(e) : f16_to_f32(e);
+                ss = fmaf(v, v, ss);
+            }
+            ss = wave_sum(ss);
+            if ((t & 63) == 0) nred[m][t >> 6] = ss;
+        }
+        __syncthreads();
+        const u32x4* wg = static_cast<const u32x4*>(na.w);
+        for (int u0 = 0; u0 < npieces; u0 += NT) {   // uniform: stage_piece shuffles across lanes
+            const int u = u0 + tid;
+            u32x4 nv = u32x4{0u, 0u, 0u, 0u};
+            if (u < npieces) {
+                const int m = u / ppr, c = u - m * ppr;
+                float tot = 0.f;
+#pragma unroll
+                for (int i = 0; i < kNormThreads / 64; ++i) tot += nred[m][i];
+                const float inv = 1.0f / sqrtf(tot / static_cast<float>(K) + na.eps);
+                const u32x4 sv = *reinterpret_cast<const u32x4*>(xs + m * ldx + c * 8);
+                const u32x4 wv = wg[c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t sw = sv[i], ww = wv[i];
+                    nv[i] = dword_map<XDT>(sw, ww, [inv](float x, float y) { return x * inv * y; });
+                }
+            }
+            stage_piece(u, nv);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < XPT; ++j) stage_piece(static_cast<int>(threadIdx.x) + j * NT, xt[j]);
+        for (int u0 = XPT * NT; u0 < npieces; u0 += NT) {
+            const int u = u0 + static_cast<int>(threadIdx.x);
+            stage_piece(u, u < npieces ? xg[u] : u32x4{0u, 0u, 0u, 0u});
+        }
     }
     for (int u = static_cast<int>(threadIdx.x); u < (K / FG) * (kRows - m_rows); u += NT) {
         const int ch = u / (kRows - m_rows), m = m_rows + (u - ch * (kRows - m_rows));
@@ -298,13 +374,13 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
 // Block shape: S waves along K per tile, P tiles per block, U k-blocks in flight.
 constexpr int kS = 4, kP = 4, kU = 4;
 
-template <int BITS, int XDT, int G>
-int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s) {
+template <int BITS, int XDT, int G, bool NORM>
+int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s, const NormArgs& na) {
     constexpr int NT = 64 * kS * kP;
     constexpr int XPT = 4;
     // the same bytes in flight per wave: four 64-wide or two 128-wide k-blocks
     constexpr int U = BlockLayout<BITS, G>::KBK == 128 ? kU / 2 : kU;
-    auto kern = qmm_gate_up_stream_kernel<BITS, XDT, G, kS, kP, U, XPT, pair_regs<G>()>;
+    auto kern = qmm_gate_up_stream_kernel<BITS, XDT, G, kS, kP, U, XPT, pair_regs<G>(), NORM>;
     const size_t lds = gate_up_lds_bytes<BITS, G>(m, w.k);
     const int res = resident_blocks(kern, NT, lds);
     if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
@@ -312,21 +388,21 @@ int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t
     const int need = (ntiles + kP - 1) / kP;
     const int blocks = need < res ? need : res;
     return static_cast<int>(launch(kern, dim3(blocks), dim3(NT), lds, s, static_cast<const uint8_t*>(w.q),
-                                   w.scale_bias, x, h, w.n, w.k, m));
+                                   w.scale_bias, x, h, w.n, w.k, m, na));
 }
 
-template <int BITS, int XDT>
-int run_gate_up_g(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s) {
+template <int BITS, int XDT, bool NORM>
+int run_gate_up_g(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s, const NormArgs& na) {
     switch (w.group) {
-        case 32: return run_gate_up<BITS, XDT, 32>(w, x, h, m, s);
-        case 64: return run_gate_up<BITS, XDT, 64>(w, x, h, m, s);
-        default: return run_gate_up<BITS, XDT, 128>(w, x, h, m, s);
+        case 32: return run_gate_up<BITS, XDT, 32, NORM>(w, x, h, m, s, na);
+        case 64: return run_gate_up<BITS, XDT, 64, NORM>(w, x, h, m, s, na);
+        default: return run_gate_up<BITS, XDT, 128, NORM>(w, x, h, m, s, na);
     }
 }
 
-template <int XDT>
-int run_gate_up_x(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s) {
-    return w.bits == 8 ? run_gate_up_g<8, XDT>(w, x, h, m, s) : run_gate_up_g<4, XDT>(w, x, h, m, s);
+template <int XDT, bool NORM>
+int run_gate_up_x(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s, const NormArgs& na) {
+    return w.bits == 8 ? run_gate_up_g<8, XDT, NORM>(w, x, h, m, s, na) : run_gate_up_g<4, XDT, NORM>(w, x, h, m, s, na);
 }
 
 }  // namespace
@@ -348,13 +424,23 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
                                                       : gate_up_lds_bytes<4, 128>(m, w.k))
                                    : (w.group == 32 ? gate_up_lds_bytes<8, 32>(m, w.k)
                                                     : gate_up_lds_bytes<8, 64>(m, w.k));
-    const size_t lds = dyn + static_cast<size_t>(kS - 1) * kP * 2 * 64 * 16 + 2 * kRows * 4;
+    const size_t lds = dyn + static_cast<size_t>(kS - 1) * kP * 2 * 64 * 16 + 2 * kRows * 4 + kRows * 4 * 4;
     return lds <= kLdsCap;
 }
 
 int launch_gate_up_mma_stream(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return act == DT_F16 ? run_gate_up_x<DT_F16>(gu, x, h, m, s) : run_gate_up_x<DT_BF16>(gu, x, h, m, s);
+    const NormArgs na{nullptr, nullptr, nullptr, 0.f};
+    return act == DT_F16 ? run_gate_up_x<DT_F16, false>(gu, x, h, m, s, na)
+                         : run_gate_up_x<DT_BF16, false>(gu, x, h, m, s, na);
+}
+
+int launch_gate_up_mma_stream_norm(const void* a, const void* b, const void* w, float eps, int m, int act,
+                                   const qdm_weight& gu, float* h, void* s_buf, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const NormArgs na{b, w, s_buf, eps};
+    return act == DT_F16 ? run_gate_up_x<DT_F16, true>(gu, a, h, m, s, na)
+                         : run_gate_up_x<DT_BF16, true>(gu, a, h, m, s, na);
 }
 
 }  // namespace qdm

@@ -66,8 +66,8 @@ def test_workload_chain(wl_index):
 
 @pytest.mark.parametrize("m", [1, 4, 16])
 def test_workload5_chain_rows(m):
-    """Llama-3-8B 4-bit: one row takes the two chained launches, several rows
-    the three launches."""
+    """Llama-3-8B 4-bit: one row on the chained streaming kernels, several rows
+    on the chained matrix-core kernels."""
     wl = W.WORKLOADS[5]
     print(f"[chain] workload 5 m={m}", flush=True)
     ow, pw = workload_case(5)
@@ -142,3 +142,47 @@ def test_chain_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager) and torch.equal(s, s_eager)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (4, 128)])
+@pytest.mark.parametrize("m", [2, 7, 16])
+def test_chain_rows(m, bits, group, act):
+    """Several rows: the norm rebuilt in every matrix-core gate/up block, s
+    through the workspace; bitwise equal to the three launches."""
+    print(f"[chain] rows m={m} bits={bits} group={group} act={act}", flush=True)
+    d, ffn = 1024, 1536
+    ow, pw = generic_case((d, m, bits), d, ffn, bits, group)
+    a = W.generic_act((m, 21), (m, d), act)
+    b = W.generic_act((m, 22), (m, d), act)
+    w = W.to_storage(np.random.default_rng(m).uniform(0.5, 1.5, d).astype(np.float32), act)
+    _chain_check(ow, pw, a, b, w, act)
+
+
+def test_chain_rows_in_place_and_graph():
+    """Several rows with s_out aliasing a and out aliasing b, then the same
+    call captured in a graph and replayed: bitwise equal to the three launches."""
+    qdm = _qdm()
+    m, d, ffn = 4, 1024, 1536
+    _, (gu, dn) = generic_case((d, m, 99), d, ffn, 4, 64)
+    a = to_device(W.generic_act((m, 31), (m, d), "bf16"))
+    b = to_device(W.generic_act((m, 32), (m, d), "bf16"))
+    w = to_device(W.to_storage(np.random.default_rng(3).uniform(0.5, 1.5, d).astype(np.float32), "bf16"))
+    s_u, n_u = qdm.add_rmsnorm(a, b, w, EPS)
+    y_u = qdm.mlp_decode(n_u, s_u, gu, dn)
+    a2, b2 = a.clone(), b.clone()
+    qdm.mlp_decode_rmsnorm(a2, b2, w, EPS, gu, dn, s_out=a2, out=b2)
+    torch.cuda.synchronize()
+    assert torch.equal(a2, s_u) and torch.equal(b2, y_u)
+    ws = torch.empty(qdm.mlp_rmsnorm_workspace_bytes(m, d, ffn, qdm.QDM_BF16), dtype=torch.uint8, device="cuda")
+    out, s = torch.empty_like(a), torch.empty_like(a)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qdm.mlp_decode_rmsnorm(a, b, w, EPS, gu, dn, workspace=ws, s_out=s, out=out)
+    for _ in range(3):
+        out.zero_()
+        s.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, y_u) and torch.equal(s, s_u)
