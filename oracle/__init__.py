@@ -23,6 +23,9 @@ What it computes (plain definitions, numpy, float64):
 * ``linear`` -- y = x W^T + b, the one-row vocabulary and attention
   projections ("MLX-LM Backend" page, the passages on vocabulary and
   attention-projection compression).
+* ``quantize_mx`` / ``dequantize_mx`` / ``decode_element`` / ``pack_mx_codes``
+  -- MXFP4 / MXFP8 block-scaled weights ("MLX-LM Backend" page, section
+  "Block-Scaled MLX Primitive"; read as the OCP Microscaling formats).
 * ``scaled_error`` -- max|out - ref| / max|ref|, the scale-normalized error
   ("Compute-Graph Fusion" page, section "Automatic Gated Epilogues").
 
@@ -38,6 +41,7 @@ from .mlp import silu, gate_up_swiglu, down_residual, mlp_decode
 from .rmsnorm import round_to_dtype, add_rmsnorm
 from .chain import mlp_decode_rmsnorm
 from .linear import linear
+from .mx import quantize_mx, dequantize_mx, decode_element, decode_scale, pack_mx_codes
 from .compare import scaled_error
 
 __all__ = [
@@ -46,4 +50,5 @@ __all__ = [
     "pack_gate_up", "pack_gate_up_scale_bias", "pack_dense_gate_up",
     "silu", "gate_up_swiglu", "down_residual", "mlp_decode",
     "round_to_dtype", "add_rmsnorm", "mlp_decode_rmsnorm", "linear", "scaled_error",
+    "quantize_mx", "dequantize_mx", "decode_element", "decode_scale", "pack_mx_codes",
 ]
