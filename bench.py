@@ -204,6 +204,7 @@ def other_configs(samples, only=None):
         return res
     res.update(projection_configs(samples, dev))
     res["group_sweep"] = group_sweep(samples, dev)
+    res.update(mx_configs(samples, dev))
     # add + RMSNorm (the row-a5 kernel) on the Llama-3.2-1B-shaped f16 row, and a launch floor
     wl = W.WORKLOADS[2]
     a, b, w = W.rmsnorm_inputs(wl)
@@ -250,6 +251,37 @@ def group_sweep(samples, dev):
             torch.cuda.empty_cache()
         res[f"workload{wi}_m1"] = row
         del g32, u32, d32
+    return res
+
+
+def mx_configs(samples, dev):
+    """The Qwen3-8B-shaped one-row MLP with MXFP8 and MXFP4 block-scaled weights, over
+    address-distinct copies of at least 2 GiB."""
+    import torch
+    import quantized_decode_mlp_amd as qdm
+    res = {}
+    wl = W.WORKLOADS[4]
+    g32, u32, d32 = W.weights_f32(wl, 0)
+    x, r = W.activations(wl, 1)
+    xd, rd = dev(x), dev(r)
+    ws = torch.empty(qdm.mlp_workspace_bytes(1, wl.ffn), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(rd)
+    for name, fmt in (("mxfp8", qdm.QDM_MXFP8), ("mxfp4", qdm.QDM_MXFP4)):
+        q, e = qdm.quantize_mx_gate_up(g32, u32, fmt)
+        dq, de = qdm.quantize_mx(d32, fmt)
+        nbytes = 2 * q.nbytes // 2 + e.nbytes + dq.nbytes + de.nbytes
+        copies = int(-(-(2 << 30) // nbytes))
+        sets = [(qdm.Weight.from_host(wl.ffn, wl.d, fmt, 32, q, None, block_scales=e),
+                 qdm.Weight.from_host(wl.d, wl.ffn, fmt, 32, dq, None, block_scales=de)) for _ in range(copies)]
+        t = graph_samples(lambda i: qdm.mlp_decode(xd, rd, *sets[i], workspace=ws, out=out), copies, samples)
+        med = float(np.median(t))
+        res[f"qwen3_8b_{name}_m1"] = {"us_per_layer": pcts(t), "weight_bytes": int(nbytes),
+                                      "weight_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                      "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                                      "copies": copies}
+        _log(f"{name}: {med:.2f} us/layer")
+        del sets
+        torch.cuda.empty_cache()
     return res
 
 

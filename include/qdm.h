@@ -35,12 +35,22 @@
  *   8  : affine uint8 codes, one per byte, row-major [n][k];
  *   4  : affine 4-bit codes, two per byte, row-major [n][k/2]; byte i of a row
  *        holds code 2i in its low nibble and code 2i+1 in its high nibble;
- *   16 : dense bf16 weights [n][k] (no scale/bias; group = 0).
+ *   16 : dense bf16 weights [n][k] (no scale/bias; group = 0);
+ *   QDM_MXFP8, QDM_MXFP4 : block-scaled weights ("MLX-LM Backend" page,
+ *        section "Block-Scaled MLX Primitive": E8M0 block scales with E4M3 or
+ *        E2M1 elements; read as the OCP Microscaling formats): blocks of 32
+ *        along k (group = 32), element codes row-major [n][k] one per byte
+ *        (E4M3) or [n][k/2] two per byte low nibble first (E2M1), and one
+ *        E8M0 byte per block in block_scales [n][k/32].
  * Affine value of code q in group j of row i:  w = scale[i][j]*q + bias[i][j]
  * with fp32 (scale, bias) stored as adjacent pairs, [n][k/group][2].
+ * MX value of element code c in block j of row i:
+ *   w = 2^(block_scales[i][j] - 127) * value(c), value from the element format
+ *   (E2M1: sign, 2 exponent bits with bias 1, 1 mantissa bit, largest 6;
+ *    E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits, largest 448).
  * Gate/up pairs are interleaved by rows: packed row 2f is gate row f and
  * packed row 2f+1 is up row f, for the codes ([ffn][2][...]) and for the
- * scale/bias pairs ([ffn][2][d/group][2]).
+ * scale/bias pairs ([ffn][2][d/group][2]) or block scales ([ffn][2][d/32]).
  */
 #ifndef QDM_H
 #define QDM_H
@@ -63,16 +73,23 @@ typedef enum qdm_status {
 
 typedef enum qdm_dtype { QDM_F32 = 0, QDM_F16 = 1, QDM_BF16 = 2 } qdm_dtype;
 
+/* Values of qdm_weight.bits besides 4, 8 and 16. */
+enum { QDM_MXFP4 = 0x104, QDM_MXFP8 = 0x108 };
+
 /* A packed weight matrix in device memory, described once per weight set and
  * reused for every call (the pages bind prepared weights once into a warmed
  * executor: "MLX-LM Backend", "Dispatch Policy").
  *   n, k        logical shape [n][k]; the contraction runs over k.  For a
  *               gate/up pair descriptor n = ffn (the number of pairs) and
  *               k = d.
- *   bits        8, 4 or 16 (see above).
- *   group       32, 64 or 128 for bits 8/4 (k % group == 0); 0 for bits 16.
+ *   bits        8, 4, 16, QDM_MXFP8 or QDM_MXFP4 (see above).
+ *   group       32, 64 or 128 for bits 8/4 (k % group == 0); 0 for bits 16;
+ *               32 for the MX formats.
  *   q           device, 16-byte aligned: packed codes or bf16 words.
- *   scale_bias  device, 8-byte aligned: fp32 pairs; NULL for bits 16.    */
+ *   scale_bias  device, 8-byte aligned: fp32 pairs; NULL for bits 16 and MX.
+ *   block_scales device: E8M0 bytes [n][k/32] for MX; NULL otherwise.
+ * MX weights are taken by the one-row calls (m = 1) whose projections run on
+ * the weight-streaming kernel; anything else returns QDM_ERR_UNSUPPORTED. */
 typedef struct qdm_weight {
     int32_t n;
     int32_t k;
@@ -80,6 +97,7 @@ typedef struct qdm_weight {
     int32_t group;
     const void* q;
     const float* scale_bias;
+    const uint8_t* block_scales;
 } qdm_weight;
 
 /* ----------------------------------------------------------------- sizes */
@@ -91,6 +109,9 @@ size_t qdm_packed_q_bytes(int32_t n, int32_t k, int32_t bits);
 /* Number of fp32 values of the scale/bias pairs of an [n][k] matrix: 2*n*k/group;
  * 0 if invalid. */
 size_t qdm_scale_bias_floats(int32_t n, int32_t k, int32_t group);
+
+/* Bytes of the E8M0 block scales of an MX [n][k] matrix: n*k/32; 0 if invalid. */
+size_t qdm_mx_scale_bytes(int32_t n, int32_t k);
 
 /* Workspace bytes qdm_mlp_decode needs for m rows: the fp32 hidden row(s)
  * h[m][ffn], rounded up to 256 bytes; 0 if invalid. */
@@ -138,6 +159,24 @@ int qdm_pack_gate_up(const uint8_t* gate_codes, const float* gate_scale, const f
                      const uint8_t* up_codes, const float* up_scale, const float* up_bias,
                      int32_t ffn, int32_t d, int32_t bits, int32_t group,
                      void* q_out, float* scale_bias_out);
+
+/* MX quantizer (the pages name the formats, not a quantizer; this is the OCP
+ * Microscaling conversion, the plain reading): per block of 32,
+ *   shared = clamp(floor(log2(max |w|)) - emax, -127, 127)   (emax 2 for E2M1,
+ *            8 for E4M3; an all-zero block takes shared = -127)
+ *   scale code = shared + 127
+ *   element = the element value nearest |w| / 2^shared (ties to the even
+ *            mantissa), saturated at the largest; the sign bit set for w < 0.
+ * w host fp32 [n][k] (k % 32 == 0) -> q_out (qdm_packed_q_bytes(n, k, format)
+ * bytes) and scales_out (qdm_mx_scale_bytes(n, k) bytes).  Bit-exact.
+ * INVALID_ARG for NULLs, bad sizes or a non-finite weight; UNSUPPORTED for a
+ * format other than QDM_MXFP4 / QDM_MXFP8. */
+int qdm_quantize_mx(const float* w, int32_t n, int32_t k, int32_t format, void* q_out, uint8_t* scales_out);
+
+/* Gate and up (each host fp32 [ffn][d]) -> interleaved MX codes [ffn][2][...]
+ * and block scales [ffn][2][d/32]. */
+int qdm_quantize_mx_gate_up(const float* w_gate, const float* w_up, int32_t ffn, int32_t d, int32_t format,
+                            void* q_out, uint8_t* scales_out);
 
 /* Dense bf16 gate and up [ffn][d] (host uint16 words) -> interleaved
  * out [ffn][2][d] (the interleaved gate/up view of "Dispatch Policy"). */

@@ -26,6 +26,7 @@ QDM_ERR_WORKSPACE = -4
 QDM_ERR_HIP = -5
 
 QDM_F32, QDM_F16, QDM_BF16 = 0, 1, 2
+QDM_MXFP4, QDM_MXFP8 = 0x104, 0x108       # qdm_weight.bits of the MX block-scaled formats
 
 # Every symbol include/qdm.h declares (checked by the tests).
 EXPORTS = (
@@ -34,6 +35,7 @@ EXPORTS = (
     "qdm_quantize_pack_gate_up", "qdm_pack_gate_up", "qdm_pack_dense_gate_up",
     "qdm_gemv_gate_up_swiglu", "qdm_gemv_down_residual", "qdm_gemv_linear", "qdm_mlp_decode",
     "qdm_add_rmsnorm", "qdm_mlp_rmsnorm_workspace_bytes", "qdm_mlp_decode_rmsnorm",
+    "qdm_mx_scale_bytes", "qdm_quantize_mx", "qdm_quantize_mx_gate_up",
     "qdm_status_string", "qdm_version",
 )
 
@@ -46,7 +48,8 @@ class QdmError(RuntimeError):
 
 class qdm_weight(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("k", ctypes.c_int32), ("bits", ctypes.c_int32),
-                ("group", ctypes.c_int32), ("q", ctypes.c_void_p), ("scale_bias", ctypes.c_void_p)]
+                ("group", ctypes.c_int32), ("q", ctypes.c_void_p), ("scale_bias", ctypes.c_void_p),
+                ("block_scales", ctypes.c_void_p)]
 
 
 def _load():
@@ -78,6 +81,9 @@ def _load():
         "qdm_mlp_rmsnorm_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int]),
         "qdm_mlp_decode_rmsnorm": (ctypes.c_int, [vp, vp, vp, f32, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
                                                   ctypes.POINTER(qdm_weight), vp, sz, vp, vp, vp]),
+        "qdm_mx_scale_bytes": (sz, [i32, i32]),
+        "qdm_quantize_mx": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
+        "qdm_quantize_mx_gate_up": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
         "qdm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "qdm_version": (ctypes.c_int, []),
     }
@@ -189,6 +195,38 @@ def quantize_pack_gate_up(w_gate, w_up, bits: int, group: int):
     return q.reshape(ffn, 2, -1), sb.reshape(ffn, 2, d // group, 2)
 
 
+def mx_scale_bytes(n: int, k: int) -> int:
+    return int(_lib.qdm_mx_scale_bytes(n, k))
+
+
+def _mx_buffers(n, k, fmt, rows_mult=1):
+    qb, eb = packed_q_bytes(n, k, fmt), mx_scale_bytes(n, k)
+    if qb == 0 or eb == 0:
+        raise QdmError(QDM_ERR_INVALID_ARG, "MX sizes")
+    return np.empty(qb * rows_mult, np.uint8), np.empty(eb * rows_mult, np.uint8)
+
+
+def quantize_mx(w, fmt: int):
+    """fp32 [n, k] -> (stored codes uint8 [n, k or k/2], E8M0 scales uint8 [n, k/32]); fmt QDM_MXFP4/8."""
+    w = _host(w, np.float32)
+    n, k = w.shape
+    q, e = _mx_buffers(n, k, fmt)
+    _check(_lib.qdm_quantize_mx(_ptr(w), n, k, fmt, _ptr(q), _ptr(e)), "qdm_quantize_mx")
+    return q.reshape(n, -1), e.reshape(n, -1)
+
+
+def quantize_mx_gate_up(w_gate, w_up, fmt: int):
+    """-> (codes uint8 [ffn, 2, ...], E8M0 scales uint8 [ffn, 2, d/32]), rows interleaved."""
+    wg, wu = _host(w_gate, np.float32), _host(w_up, np.float32)
+    if wg.shape != wu.shape:
+        raise ValueError("gate and up shapes differ")
+    ffn, d = wg.shape
+    q, e = _mx_buffers(ffn, d, fmt, rows_mult=2)
+    _check(_lib.qdm_quantize_mx_gate_up(_ptr(wg), _ptr(wu), ffn, d, fmt, _ptr(q), _ptr(e)),
+           "qdm_quantize_mx_gate_up")
+    return q.reshape(ffn, 2, -1), e.reshape(ffn, 2, -1)
+
+
 def pack_gate_up(gate_codes, gate_scale, gate_bias, up_codes, up_scale, up_bias, bits: int, group: int):
     gc, uc = _host(gate_codes, np.uint8), _host(up_codes, np.uint8)
     gs, gb = _host(gate_scale, np.float32), _host(gate_bias, np.float32)
@@ -247,27 +285,33 @@ class Weight:
     k: int
     bits: int
     group: int
-    q: object                       # torch uint8 (affine) or int16/uint8 view (dense) on device
-    scale_bias: Optional[object]    # torch float32 on device, or None for dense
+    q: object                       # torch uint8 (affine, MX) or int16/uint8 view (dense) on device
+    scale_bias: Optional[object]    # torch float32 on device, or None for dense and MX
+    block_scales: Optional[object] = None   # torch uint8 E8M0 scales on device (MX), else None
     _desc: qdm_weight = field(default=None, repr=False)
 
     def __post_init__(self):
         self._desc = qdm_weight(self.n, self.k, self.bits, self.group,
                                 ctypes.c_void_p(self.q.data_ptr()).value,
                                 None if self.scale_bias is None else
-                                ctypes.c_void_p(self.scale_bias.data_ptr()).value)
+                                ctypes.c_void_p(self.scale_bias.data_ptr()).value,
+                                None if self.block_scales is None else
+                                ctypes.c_void_p(self.block_scales.data_ptr()).value)
 
     @property
     def descriptor(self) -> qdm_weight:
         return self._desc
 
     @staticmethod
-    def from_host(n, k, bits, group, q: np.ndarray, scale_bias: Optional[np.ndarray], device="cuda"):
+    def from_host(n, k, bits, group, q: np.ndarray, scale_bias: Optional[np.ndarray], device="cuda",
+                  block_scales: Optional[np.ndarray] = None):
         torch = _torch()
         qt = torch.from_numpy(np.ascontiguousarray(q).view(np.uint8).reshape(-1)).to(device)
         sbt = None if scale_bias is None else \
             torch.from_numpy(np.ascontiguousarray(scale_bias, dtype=np.float32).reshape(-1)).to(device)
-        return Weight(n, k, bits, group, qt, sbt)
+        bst = None if block_scales is None else \
+            torch.from_numpy(np.ascontiguousarray(block_scales, dtype=np.uint8).reshape(-1)).to(device)
+        return Weight(n, k, bits, group, qt, sbt, bst)
 
 
 def gemv_gate_up_swiglu(x, gate_up: Weight, h_out=None, stream=None):
@@ -372,5 +416,5 @@ __all__ = [
     "status_string", "version", "packed_q_bytes", "scale_bias_floats", "mlp_workspace_bytes",
     "quantize_affine", "pack_rows", "quantize_pack_rows", "quantize_pack_gate_up", "pack_gate_up",
     "pack_dense_gate_up", "gemv_gate_up_swiglu", "gemv_down_residual", "gemv_linear", "mlp_decode", "add_rmsnorm",
-    "mlp_rmsnorm_workspace_bytes", "mlp_decode_rmsnorm",
+    "mlp_rmsnorm_workspace_bytes", "mlp_decode_rmsnorm", "mx_scale_bytes", "quantize_mx", "quantize_mx_gate_up",
 ]

@@ -220,11 +220,17 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
             switch (w.bits) {
                 case 8: return run_stream<8, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
                 case 4: return run_stream<4, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
+                case QDM_MXFP8:
+                    return run_stream<QDM_MXFP8, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
+                case QDM_MXFP4:
+                    return run_stream<QDM_MXFP4, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
                 default: return run_stream<16, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
             }
         }
+        if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);   // MX: streaming kernel only
         return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s, n_out);
     }
+    if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);
     // 2..16 rows on the matrix cores.  Gate/up with 8/4-bit weights and 16-bit
     // activations, down with 8/4-bit weights and a 16-bit output: the
     // weight-streaming kernels (down split along K).  Otherwise the tile-per-block
@@ -268,9 +274,14 @@ int run_linear(const qdm_weight& w, const void* x, int m, const void* bias, void
         switch (w.bits) {
             case 8: return run_stream<8, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
             case 4: return run_stream<4, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
+            case QDM_MXFP8:
+                return run_stream<QDM_MXFP8, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
+            case QDM_MXFP4:
+                return run_stream<QDM_MXFP4, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
             default: return run_stream<16, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
         }
     }
+    if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);
     const size_t xe = XDT == DT_F32 ? 4 : 2;
     for (int m0 = 0; m0 < m; m0 += 4) {
         const int mr = m - m0 < 4 ? m - m0 : 4;
@@ -284,6 +295,11 @@ int run_linear(const qdm_weight& w, const void* x, int m, const void* bias, void
 }
 
 }  // namespace
+
+bool stream_supported(const qdm_weight& w, int xb) {
+    StreamSplit sp;
+    return stream_split(w.bits, w.k, xb, sp);
+}
 
 int launch_linear(const void* x, int m, int act, const qdm_weight& w, const void* bias, void* out, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -13,6 +13,9 @@ int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, f
                           void* stream);
 int launch_down_residual(const float* h, const void* r, int m, int act, const qdm_weight& dn,
                          void* out, void* stream);
+// True when one row of x (xb bytes per element) times w runs on the
+// weight-streaming kernel (the only kernel that takes MX weights).
+bool stream_supported(const qdm_weight& w, int xb);
 // A projection out[m][n] = x W^T (+ bias[n] when bias is not null), act dtype in and out.
 int launch_linear(const void* x, int m, int act, const qdm_weight& w, const void* bias, void* out, void* stream);
 // Few-row (2..16) projections on the matrix cores (qdm_mfma.hip).

@@ -1,4 +1,5 @@
-// Host-side affine quantization and packing (ahead of time, once per weight set).
+// Host-side affine and MX block-scaled quantization and packing (ahead of
+// time, once per weight set).
 //
 // Pages: meTile docs, "MLX-LM Backend" -- affine formats keep a scale and a bias
 // per group of 32/64/128 along the input dim; the 4-bit repack keeps nibbles,
@@ -105,9 +106,112 @@ bool codes_in_range(const uint8_t* codes, int64_t count, int32_t bits) {
     return true;
 }
 
+// MX block-scaled formats: blocks of 32 along k, an E8M0 scale per block,
+// E2M1 (MXFP4) or E4M3 (MXFP8) elements -- the OCP Microscaling formats the
+// pages' MXFP4 / MXFP8 name ("MLX-LM Backend", "Block-Scaled MLX Primitive").
+constexpr int32_t kMxBlock = 32;
+
+struct MxFormat {
+    int eb, mb, bias, emax;   // exponent bits, mantissa bits, exponent bias, largest normal exponent
+    double vmax;              // largest element magnitude
+};
+
+inline bool is_mx(int32_t bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
+
+inline MxFormat mx_format(int32_t bits) {
+    return bits == QDM_MXFP4 ? MxFormat{2, 1, 1, 2, 6.0} : MxFormat{4, 3, 7, 8, 448.0};
+}
+
+// |t| rounded to the element grid (ties to even mantissa), saturated at vmax.
+inline double mx_round(double t, const MxFormat& f) {
+    if (t == 0.0) return 0.0;
+    int ex = 0;
+    std::frexp(t, &ex);                            // t = m * 2^ex, 0.5 <= m < 1
+    const int e = std::max(ex - 1, 1 - f.bias);    // subnormals share the smallest normal exponent
+    const double quantum = std::ldexp(1.0, e - f.mb);
+    const double r = std::nearbyint(t / quantum) * quantum;
+    return r > f.vmax ? f.vmax : r;
+}
+
+// A grid magnitude -> its sign-less element code.
+inline uint32_t mx_encode(double mag, const MxFormat& f) {
+    if (mag == 0.0) return 0;
+    int ex = 0;
+    std::frexp(mag, &ex);
+    const int e = ex - 1, emin = 1 - f.bias;
+    if (e < emin) return static_cast<uint32_t>(std::nearbyint(mag / std::ldexp(1.0, emin - f.mb)));
+    const uint32_t m = static_cast<uint32_t>(std::nearbyint((mag / std::ldexp(1.0, e) - 1.0) * (1 << f.mb)));
+    return (static_cast<uint32_t>(e + f.bias) << f.mb) | m;
+}
+
+// Quantizes and stores one row: q_row gets k (MXFP8) or k/2 (MXFP4) bytes, e_row k/32 scale codes.
+void quantize_mx_row(const float* w, int32_t k, int32_t bits, uint8_t* q_row, uint8_t* e_row, uint8_t* scratch) {
+    const MxFormat f = mx_format(bits);
+    const uint32_t sign = 1u << (f.eb + f.mb);
+    for (int32_t b = 0; b < k / kMxBlock; ++b) {
+        const float* v = w + static_cast<int64_t>(b) * kMxBlock;
+        float amax = 0.0f;
+        for (int32_t i = 0; i < kMxBlock; ++i) amax = std::max(amax, std::fabs(v[i]));
+        int shared = -127;
+        if (amax > 0.0f) {
+            int ex = 0;
+            std::frexp(static_cast<double>(amax), &ex);
+            shared = std::min(127, std::max(-127, ex - 1 - f.emax));
+        }
+        e_row[b] = static_cast<uint8_t>(shared + 127);
+        for (int32_t i = 0; i < kMxBlock; ++i) {
+            const double t = std::ldexp(std::fabs(static_cast<double>(v[i])), -shared);
+            const uint32_t c = mx_encode(mx_round(t, f), f) | (v[i] < 0.0f ? sign : 0u);
+            scratch[static_cast<int64_t>(b) * kMxBlock + i] = static_cast<uint8_t>(c);
+        }
+    }
+    pack_row_codes(scratch, k, bits == QDM_MXFP4 ? 4 : 8, q_row);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t qdm_mx_scale_bytes(int32_t n, int32_t k) {
+    if (n <= 0 || k <= 0 || k % kMxBlock) return 0;
+    return static_cast<size_t>(n) * static_cast<size_t>(k / kMxBlock);
+}
+
+int qdm_quantize_mx(const float* w, int32_t n, int32_t k, int32_t format, void* q_out, uint8_t* scales_out) {
+    if (!w || !q_out || !scales_out || n <= 0 || k <= 0) return QDM_ERR_INVALID_ARG;
+    if (!is_mx(format)) return QDM_ERR_UNSUPPORTED;
+    if (k % kMxBlock) return QDM_ERR_INVALID_ARG;
+    if (!all_finite(w, static_cast<int64_t>(n) * k)) return QDM_ERR_INVALID_ARG;
+    const int64_t rb = format == QDM_MXFP4 ? k / 2 : k;
+    const int32_t nb = k / kMxBlock;
+    auto* q = static_cast<uint8_t*>(q_out);
+    parallel_rows(n, k, [&](int64_t b, int64_t e) {
+        std::vector<uint8_t> scratch(static_cast<size_t>(k));
+        for (int64_t i = b; i < e; ++i) quantize_mx_row(w + i * k, k, format, q + i * rb, scales_out + i * nb, scratch.data());
+    });
+    return QDM_OK;
+}
+
+int qdm_quantize_mx_gate_up(const float* w_gate, const float* w_up, int32_t ffn, int32_t d, int32_t format,
+                            void* q_out, uint8_t* scales_out) {
+    if (!w_gate || !w_up || !q_out || !scales_out || ffn <= 0 || d <= 0) return QDM_ERR_INVALID_ARG;
+    if (!is_mx(format)) return QDM_ERR_UNSUPPORTED;
+    if (d % kMxBlock) return QDM_ERR_INVALID_ARG;
+    const int64_t nd = static_cast<int64_t>(ffn) * d;
+    if (!all_finite(w_gate, nd) || !all_finite(w_up, nd)) return QDM_ERR_INVALID_ARG;
+    const int64_t rb = format == QDM_MXFP4 ? d / 2 : d;
+    const int32_t nb = d / kMxBlock;
+    auto* q = static_cast<uint8_t*>(q_out);
+    parallel_rows(ffn, 2 * static_cast<int64_t>(d), [&](int64_t b, int64_t e) {
+        std::vector<uint8_t> scratch(static_cast<size_t>(d));
+        for (int64_t r = b; r < e; ++r) {
+            quantize_mx_row(w_gate + r * d, d, format, q + (2 * r) * rb, scales_out + (2 * r) * nb, scratch.data());
+            quantize_mx_row(w_up + r * d, d, format, q + (2 * r + 1) * rb, scales_out + (2 * r + 1) * nb,
+                            scratch.data());
+        }
+    });
+    return QDM_OK;
+}
 
 size_t qdm_packed_q_bytes(int32_t n, int32_t k, int32_t bits) {
     if (n <= 0 || k <= 0) return 0;
@@ -115,6 +219,8 @@ size_t qdm_packed_q_bytes(int32_t n, int32_t k, int32_t bits) {
     if (bits == 8) return nk;
     if (bits == 4) return (k % 2) ? 0 : nk / 2;
     if (bits == 16) return nk * 2;
+    if (bits == QDM_MXFP8) return nk;
+    if (bits == QDM_MXFP4) return (k % 2) ? 0 : nk / 2;
     return 0;
 }
 

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qdm_device.h"
 #include "qdm_internal.h"
 #include "qdm_launch.h"
@@ -77,9 +79,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
 
+// BITS is the weight format: 4 / 8 (affine), 16 (dense bf16), QDM_MXFP4 /
+// QDM_MXFP8 (block-scaled; their low byte is the code width).
+constexpr bool is_mx(int bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
+constexpr int code_bits(int bits) { return bits & 0xff; }
+
 template <int BITS>
 struct StreamShape {
-    static constexpr int E = 128 / BITS;                              // codes per 16-byte chunk
+    static constexpr int E = 128 / code_bits(BITS);                   // codes per 16-byte chunk
     static constexpr int TW_MAX = 64 / E;                             // K-tiles per wave at most
 };
 
@@ -100,7 +107,9 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     constexpr int E = StreamShape<BITS>::E;
     constexpr int EPD = E / 4;
     constexpr int NV = GU ? 2 : 1;
-    constexpr bool AFFINE = BITS != 16;
+    constexpr bool MX = is_mx(BITS);
+    constexpr int CB = code_bits(BITS);
+    constexpr bool AFFINE = BITS == 4 || BITS == 8;
     constexpr int NT = 64 * S * P;
     constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
     constexpr bool NORM = EPI == kEpiChain && GU;   // the activation row is rmsnorm(a + b) * w
@@ -115,9 +124,10 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     // wave-uniform by construction; readfirstlane lets the compiler keep it scalar
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wv % S, p = wv / S;
-    const uint32_t rb = static_cast<uint32_t>(k) * BITS / 8;   // bytes per packed row
+    const uint32_t rb = static_cast<uint32_t>(k) * CB / 8;   // bytes per packed row
     const int C = static_cast<int>(rb >> 4);
     const int ng = AFFINE ? (k >> gshift) : 0;
+    const int nbk = MX ? (k >> 5) : 0;                            // MX: scale bytes per row
     const int GP = static_cast<int>(gridDim.x) * P;
     const int g0 = static_cast<int>(blockIdx.x) * P + p;
     const int rounds = (n_out - static_cast<int>(blockIdx.x) * P + GP - 1) / GP;   // same for every wave
@@ -154,25 +164,29 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         vj[j] = c < C;
         const uint32_t cc = static_cast<uint32_t>(vj[j] ? c : C - 1);
         qoff[j] = cc * 16u;
-        soff[j] = AFFINE ? ((cc * E) >> gshift) * 8u : 0u;
+        soff[j] = AFFINE ? ((cc * E) >> gshift) * 8u : MX ? (cc * E) >> 5 : 0u;
     }
 
+    // per chunk: the affine (scale, bias) pair, or the MX block's E8M0 code
+    using ChunkScale = typename std::conditional<MX, uint32_t, f32x2>::type;
     u32x4 wbuf[NV][TW];
-    f32x2 pbuf[NV][TW];
+    ChunkScale pbuf[NV][TW];
 
     // loads of group grp (rows clamped; a stream past its last group reloads row n_out - 1)
-    auto issue = [&](u32x4 (&wq)[NV][TW], f32x2 (&pp)[NV][TW], int grp) {
+    auto issue = [&](u32x4 (&wq)[NV][TW], ChunkScale (&pp)[NV][TW], int grp) {
         const uint32_t row = static_cast<uint32_t>(min(grp, n_out - 1));
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const uint32_t prow = GU ? 2u * row + v : row;
             const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
-            const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * ng * 8u;
+            const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * (MX ? nbk : ng * 8);
 #pragma unroll
             for (int j = 0; j < TW; ++j) {
                 wq[v][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + qoff[j]));
                 if constexpr (AFFINE)
                     pp[v][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + soff[j]));
+                else if constexpr (MX)
+                    pp[v][j] = __builtin_nontemporal_load(srow + soff[j]);
             }
         }
     };
@@ -251,8 +265,14 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     // offset's share (1024 or 1 times the chunk's scaled activation sum) is
     // taken off per chunk before the group scale applies, and the powers of
     // two come off once per row.  DM 2 (bf16 weights, bf16 activations):
-    // v_dot2_f32_bf16 straight on the packed words.
-    constexpr int DM = (AFFINE && XDT != DT_F32) ? 1 : (BITS == 16 && XDT == DT_BF16) ? 2 : 0;
+    // v_dot2_f32_bf16 straight on the packed words.  MX weights: the hardware
+    // converts element pairs exactly (E4M3 bytes 0,1 / 2,3 of a dword, or an
+    // E2M1 byte's low and high nibble) -- DM 3 to f16 pairs for v_dot2 against
+    // the activations scaled to f16 as in DM 1 (no offset), DM 4 to fp32 for
+    // FMAs with fp32 activations; the block's E8M0 scale multiplies each
+    // chunk's dot product.
+    constexpr int DM = MX ? (XDT == DT_F32 ? 4 : 3)
+                          : (AFFINE && XDT != DT_F32) ? 1 : (BITS == 16 && XDT == DT_BF16) ? 2 : 0;
     float xv[TW][E];
     float xs[TW];
 #pragma unroll
@@ -261,7 +281,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         const int c = (ks * TW + j) * 64 + lane;
         if (vj[j]) {
             load_vec<XDT, E>(xlds, static_cast<int64_t>(c) * E, xv[j]);
-            if constexpr (DM != 1) {   // DM 1 takes the sum from the f16 pairs below
+            if constexpr (DM == 0 || DM == 2) {   // DM 1 takes the sum from the f16 pairs below
 #pragma unroll
                 for (int e = 0; e < E; ++e) xs[j] += xv[j][e];
             }
@@ -270,7 +290,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
             for (int e = 0; e < E; ++e) xv[j][e] = 0.f;
         }
     }
-    uint32_t xp[TW][DM == 0 ? 1 : E / 2];   // packed 16-bit activation pairs (DM 1, 2)
+    uint32_t xp[TW][DM == 0 || DM == 4 ? 1 : E / 2];   // packed 16-bit activation pairs (DM 1, 2, 3)
     float xoff[TW];                         // DM 1: the offset's share of a chunk's dot product
     int nsg = 0;                            // DM 1: -sg (+4 for 4-bit codes, which enter as n/16)
     if constexpr (DM == 1) {
@@ -307,6 +327,30 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                                            false);
             xoff[j] = (BITS == 8 ? 1024.f : 1.f) * t;
             xs[j] = __builtin_amdgcn_ldexpf(t, -sg);
+        }
+    } else if constexpr (DM == 3) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < TW; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(xv[j][e]));
+        const int sg = 15 - __builtin_amdgcn_frexp_expf(m);
+        nsg = -sg;
+#pragma unroll
+        for (int j = 0; j < TW; ++j) {
+            _Float16 hv[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) hv[e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(xv[j][e], sg));
+            // pairs in the conversions' order: E4M3 (4i+2h, 4i+2h+1), E2M1 (8i+2h, 8i+2h+1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int h = 0; h < E / 8; ++h) {
+                    const int a = CB == 8 ? 4 * i + 2 * h : 8 * i + 2 * h;
+                    xp[j][i * (E / 8) + h] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[a])) |
+                                             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[a + 1])) << 16);
+                }
+            }
         }
     } else if constexpr (DM == 2) {
 #pragma unroll
@@ -355,7 +399,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         __syncthreads();
     };
 
-    auto finish = [&](const u32x4 (&wq)[NV][TW], const f32x2 (&pp)[NV][TW], int grp, int slot) {
+    auto finish = [&](const u32x4 (&wq)[NV][TW], const ChunkScale (&pp)[NV][TW], int grp, int slot) {
         if (grp >= n_out) return;   // this stream is past its last group (wave-uniform)
         float tot[NV];
 #pragma unroll
@@ -386,6 +430,46 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                     } else if constexpr (DM == 2) {
                         dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, word),
                                                               __builtin_bit_cast(b16x2, xp[j][i]), dot, false);
+                    } else if constexpr (DM == 3 && CB == 8) {
+                        const auto c01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+                        const auto c23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c01), __builtin_bit_cast(h16x2, xp[j][2 * i]),
+                                                     dot, false);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c23),
+                                                     __builtin_bit_cast(h16x2, xp[j][2 * i + 1]), dot, false);
+                    } else if constexpr (DM == 3) {
+                        const auto c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0);
+                        const auto c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1);
+                        const auto c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2);
+                        const auto c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c0), __builtin_bit_cast(h16x2, xp[j][4 * i]),
+                                                     dot, false);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c1),
+                                                     __builtin_bit_cast(h16x2, xp[j][4 * i + 1]), dot, false);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c2),
+                                                     __builtin_bit_cast(h16x2, xp[j][4 * i + 2]), dot, false);
+                        dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c3),
+                                                     __builtin_bit_cast(h16x2, xp[j][4 * i + 3]), dot, false);
+                    } else if constexpr (DM == 4 && CB == 8) {
+                        const f32x2 f01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);
+                        const f32x2 f23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, true);
+                        dot = fmaf(f01.x, xv[j][4 * i], dot);
+                        dot = fmaf(f01.y, xv[j][4 * i + 1], dot);
+                        dot = fmaf(f23.x, xv[j][4 * i + 2], dot);
+                        dot = fmaf(f23.y, xv[j][4 * i + 3], dot);
+                    } else if constexpr (DM == 4) {
+                        const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+                        const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+                        const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+                        const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+                        dot = fmaf(f0.x, xv[j][8 * i], dot);
+                        dot = fmaf(f0.y, xv[j][8 * i + 1], dot);
+                        dot = fmaf(f1.x, xv[j][8 * i + 2], dot);
+                        dot = fmaf(f1.y, xv[j][8 * i + 3], dot);
+                        dot = fmaf(f2.x, xv[j][8 * i + 4], dot);
+                        dot = fmaf(f2.y, xv[j][8 * i + 5], dot);
+                        dot = fmaf(f3.x, xv[j][8 * i + 6], dot);
+                        dot = fmaf(f3.y, xv[j][8 * i + 7], dot);
                     } else {
 #pragma unroll
                         for (int e = 0; e < EPD; ++e) {
@@ -397,7 +481,11 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                         }
                     }
                 }
-                if constexpr (AFFINE) {
+                if constexpr (MX) {
+                    // E8M0 code e is 2^(e - 127): e in the fp32 exponent field, e = 0 the subnormal 2^-127
+                    const uint32_t e8 = pp[v][j];
+                    acc = fmaf(__uint_as_float(e8 ? e8 << 23 : 0x00400000u), dot, acc);
+                } else if constexpr (AFFINE) {
                     const float sc = pp[v][j].x, bi = pp[v][j].y;
                     if constexpr (DM == 1) {
                         acc = fmaf(sc, dot - xoff[j], acc);
@@ -410,6 +498,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                 }
             }
             if constexpr (DM == 1) acc = __builtin_amdgcn_ldexpf(acc, nsg) + acc2;
+            if constexpr (DM == 3) acc = __builtin_amdgcn_ldexpf(acc, nsg);
             tot[v] = wave_total(acc);
         }
         if constexpr (S == 1) {
@@ -445,9 +534,10 @@ struct StreamSplit { int s, tw; };
 
 bool stream_split(int bits, int k, int xb, StreamSplit& out) {
     if (static_cast<int64_t>(k) * xb > kStreamLds) return false;
-    const int64_t rb = static_cast<int64_t>(k) * bits / 8;
+    const int cb = code_bits(bits);
+    const int64_t rb = static_cast<int64_t>(k) * cb / 8;
     const int t = static_cast<int>(((rb >> 4) + 63) >> 6);
-    const int tw_max = bits == 8 ? 4 : bits == 4 ? 2 : 8;
+    const int tw_max = cb == 8 ? 4 : cb == 4 ? 2 : 8;
     if (t <= 3 || (t % 2 == 1 && t <= 8)) { out = {t, 1}; return true; }
     if (t <= 16) { out = {(t + 1) / 2, 2}; return true; }
     const int tw = (t + 7) / 8;
@@ -478,8 +568,10 @@ int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, 
         if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
         const int need = (n_out + P - 1) / P;
         const int blocks = need < res ? need : res;
+        // MX: the block scales ride in the scale/bias argument (the kernel reads bytes)
+        const float* sbp = is_mx(BITS) ? reinterpret_cast<const float*>(w.block_scales) : w.scale_bias;
         return static_cast<int>(launch(kern, dim3(blocks), dim3(64 * S * P), lds, s,
-                                       static_cast<const uint8_t*>(w.q), w.scale_bias, x, r, out, n_out, k,
+                                       static_cast<const uint8_t*>(w.q), sbp, x, r, out, n_out, k,
                                        gshift_of(w.group), ch));
     }
 }

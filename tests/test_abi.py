@@ -124,6 +124,25 @@ def test_mlp_rejects():
     assert f(out=ODD) == q.QDM_ERR_ALIGNMENT
 
 
+def test_mx_weight_rejects():
+    """MX descriptors: group 32 and block scales required; only one row on the
+    streaming kernel (several rows are rejected before anything runs)."""
+    X, OUT = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+
+    def mxw(n=256, k=512, bits=q.QDM_MXFP8, group=32, bs=FAKE):
+        return q.qdm_weight(n, k, bits, group, FAKE.value, None, bs.value if bs else None)
+
+    def lin(w, m=1):
+        return L.qdm_gemv_linear(X, m, q.QDM_BF16, ctypes.byref(w), None, OUT, None)
+
+    assert lin(mxw(group=64)) == q.QDM_ERR_UNSUPPORTED
+    assert lin(mxw(bs=None)) == q.QDM_ERR_INVALID_ARG
+    assert lin(mxw(k=500)) == q.QDM_ERR_INVALID_ARG
+    assert lin(mxw(), m=2) == q.QDM_ERR_UNSUPPORTED
+    assert lin(mxw(k=65536)) == q.QDM_ERR_UNSUPPORTED                # x does not fit the LDS stage
+    assert lin(mxw(bits=q.QDM_MXFP4), m=16) == q.QDM_ERR_UNSUPPORTED
+
+
 def test_linear_rejects():
     X, BIAS, OUT = (ctypes.c_void_p(0x10000 * i) for i in range(1, 4))
 

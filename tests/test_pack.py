@@ -116,3 +116,59 @@ def test_fuzz_bit_exact(bits, group, n, ng, seed, mode):
     _assert_same_f32(sbp, sbp2)
     c2, s2, b2 = q.quantize_affine(w, bits, group)
     assert np.array_equal(c, c2)
+
+
+# ------------------------------------------------------------------ MX block-scaled
+
+MX = [(q.QDM_MXFP4, "mxfp4"), (q.QDM_MXFP8, "mxfp8")]
+
+
+@pytest.mark.parametrize("fmt,name", MX)
+def test_mx_workload_shapes_bit_exact(fmt, name):
+    for wl, rows in ((4, 128), (5, 96), (2, 128)):
+        w = W.weight_f32(W.WORKLOADS[wl], "w_gate")[:rows]
+        c, e = oracle.quantize_mx(w, name)
+        q1, e1 = q.quantize_mx(w, fmt)
+        assert np.array_equal(q1, oracle.pack_mx_codes(c, name))
+        assert np.array_equal(e1, e)
+
+
+@pytest.mark.parametrize("fmt,name", MX)
+def test_mx_edge_values_bit_exact(fmt, name):
+    rng = np.random.default_rng(11)
+    w = rng.normal(size=(8, 128)).astype(np.float32)
+    w[0, :32] = 0.0                                   # zero block
+    w[1, :32] = -0.0
+    w[1, 32:64] = np.float32(1e-42)                   # subnormal fp32 inputs
+    w[2, :32] = np.float32(3.0e38)                    # near the fp32 maximum
+    w[2, 32:64] = rng.normal(size=32).astype(np.float32) * np.float32(2.0 ** -130)
+    w[3, :32] = np.tile(np.array([6.0, 2.5, 3.5, 5.0, -0.2, 0.25, 0.75, 7.5], np.float32), 4)
+    w[4] = np.round(w[4] * 8) / 8                     # many ties
+    c, e = oracle.quantize_mx(w, name)
+    q1, e1 = q.quantize_mx(w, fmt)
+    assert np.array_equal(q1, oracle.pack_mx_codes(c, name))
+    assert np.array_equal(e1, e)
+
+
+@pytest.mark.parametrize("fmt,name", MX)
+def test_mx_gate_up_interleave(fmt, name):
+    wg = W.generic_weights((3, fmt), 24, 256, 0.02)
+    wu = W.generic_weights((4, fmt), 24, 256, 0.02)
+    q1, e1 = q.quantize_mx_gate_up(wg, wu, fmt)
+    for v, w in enumerate((wg, wu)):
+        c, e = oracle.quantize_mx(w, name)
+        assert np.array_equal(q1[:, v], oracle.pack_mx_codes(c, name))
+        assert np.array_equal(e1[:, v], e)
+
+
+def test_mx_rejects():
+    w = np.zeros((2, 64), np.float32)
+    L = q._lib
+    qb, eb = np.empty(128, np.uint8), np.empty(4, np.uint8)
+    assert L.qdm_quantize_mx(q._ptr(w), 2, 64, 0x105, q._ptr(qb), q._ptr(eb)) == q.QDM_ERR_UNSUPPORTED
+    assert L.qdm_quantize_mx(q._ptr(w), 2, 48, q.QDM_MXFP8, q._ptr(qb), q._ptr(eb)) == q.QDM_ERR_INVALID_ARG
+    w[1, 3] = np.nan
+    assert L.qdm_quantize_mx(q._ptr(w), 2, 64, q.QDM_MXFP8, q._ptr(qb), q._ptr(eb)) == q.QDM_ERR_INVALID_ARG
+    assert q.mx_scale_bytes(4096, 12288) == 4096 * 384
+    assert q.mx_scale_bytes(4, 48) == 0
+    assert q.packed_q_bytes(4, 64, q.QDM_MXFP4) == 128 and q.packed_q_bytes(4, 64, q.QDM_MXFP8) == 256
