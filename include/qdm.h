@@ -89,7 +89,10 @@ enum { QDM_MXFP4 = 0x104, QDM_MXFP8 = 0x108 };
  *   scale_bias  device, 8-byte aligned: fp32 pairs; NULL for bits 16 and MX.
  *   block_scales device: E8M0 bytes [n][k/32] for MX; NULL otherwise.
  * MX weights are taken by the one-row calls (m = 1) whose projections run on
- * the weight-streaming kernel; anything else returns QDM_ERR_UNSUPPORTED. */
+ * the weight-streaming kernel, and by the MLP calls with 2..16 rows and a
+ * 16-bit act dtype whose projections run on the matrix-core streaming
+ * kernels; anything else (qdm_gemv_linear with m > 1 among it) returns
+ * QDM_ERR_UNSUPPORTED. */
 typedef struct qdm_weight {
     int32_t n;
     int32_t k;

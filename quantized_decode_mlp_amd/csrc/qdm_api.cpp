@@ -43,10 +43,15 @@ int hip_status(int e) { return e == 0 ? QDM_OK : QDM_ERR_HIP; }
 
 bool is_mx(int32_t bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
 
-// MX weights run only as one row on the weight-streaming kernel (x of xb bytes).
-int check_mx_rows(const qdm_weight* w, int32_t m, int xb) {
+// MX weights: one row on the weight-streaming kernel (x of xb bytes); 2..16
+// rows of a gate/up (kind 0) or down (kind 1) projection on the matrix-core
+// streaming kernels (16-bit activations / outputs); nothing else.
+int check_mx_rows(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
     if (!is_mx(w->bits)) return QDM_OK;
-    return (m == 1 && qdm::stream_supported(*w, xb)) ? QDM_OK : QDM_ERR_UNSUPPORTED;
+    if (m == 1) return qdm::stream_supported(*w, xb) ? QDM_OK : QDM_ERR_UNSUPPORTED;
+    if (kind == 0) return qdm::mma_stream_gate_up_supported(*w, m, act) ? QDM_OK : QDM_ERR_UNSUPPORTED;
+    if (kind == 1) return qdm::mma_stream_down_supported(*w, m, act) ? QDM_OK : QDM_ERR_UNSUPPORTED;
+    return QDM_ERR_UNSUPPORTED;
 }
 
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -69,7 +74,7 @@ int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act, const qdm_w
     if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
     if (int e = check_rows(m)) return e;
     if (int e = check_weight(gate_up)) return e;
-    if (int e = check_mx_rows(gate_up, m, act == QDM_F32 ? 4 : 2)) return e;
+    if (int e = check_mx_rows(gate_up, m, act == QDM_F32 ? 4 : 2, act, 0)) return e;
     if (!aligned(x, 16) || !aligned(h_out, 16)) return QDM_ERR_ALIGNMENT;
     return hip_status(qdm::launch_gate_up_swiglu(x, m, act, *gate_up, h_out, stream));
 }
@@ -81,7 +86,7 @@ int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype a
     if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
     if (int e = check_rows(m)) return e;
     if (int e = check_weight(down)) return e;
-    if (int e = check_mx_rows(down, m, 4)) return e;
+    if (int e = check_mx_rows(down, m, 4, act, 1)) return e;
     if (!aligned(h, 16) || !aligned(r, 16) || !aligned(out, 16)) return QDM_ERR_ALIGNMENT;
     return hip_status(qdm::launch_down_residual(h, r, m, act, *down, out, stream));
 }
@@ -93,7 +98,7 @@ int qdm_gemv_linear(const void* x, int32_t m, qdm_dtype act, const qdm_weight* w
     if (!valid_dtype(act)) return QDM_ERR_INVALID_ARG;
     if (int e = check_rows(m)) return e;
     if (int e = check_weight(w)) return e;
-    if (int e = check_mx_rows(w, m, act == QDM_F32 ? 4 : 2)) return e;
+    if (int e = check_mx_rows(w, m, act == QDM_F32 ? 4 : 2, act, 2)) return e;
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(bias, 16)) return QDM_ERR_ALIGNMENT;
     return hip_status(qdm::launch_linear(x, m, act, *w, bias, out, stream));
 }
@@ -108,8 +113,8 @@ int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
     if (int e = check_weight(down)) return e;
     if (gate_up->k != down->n || gate_up->n != down->k) return QDM_ERR_INVALID_ARG;
     if (gate_up->bits != down->bits) return QDM_ERR_UNSUPPORTED;
-    if (int e = check_mx_rows(gate_up, m, act == QDM_F32 ? 4 : 2)) return e;
-    if (int e = check_mx_rows(down, m, 4)) return e;
+    if (int e = check_mx_rows(gate_up, m, act == QDM_F32 ? 4 : 2, act, 0)) return e;
+    if (int e = check_mx_rows(down, m, 4, act, 1)) return e;
     if (!workspace || workspace_bytes < qdm_mlp_workspace_bytes(m, gate_up->n)) return QDM_ERR_WORKSPACE;
     if (workspace == out) return QDM_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(r, 16) || !aligned(out, 16) || !aligned(workspace, 16))
@@ -136,8 +141,8 @@ int qdm_mlp_decode_rmsnorm(const void* a, const void* b, const void* norm_w, flo
     if (int e = check_weight(down)) return e;
     if (gate_up->k != down->n || gate_up->n != down->k) return QDM_ERR_INVALID_ARG;
     if (gate_up->bits != down->bits) return QDM_ERR_UNSUPPORTED;
-    if (int e = check_mx_rows(gate_up, m, act == QDM_F32 ? 4 : 2)) return e;
-    if (int e = check_mx_rows(down, m, 4)) return e;
+    if (int e = check_mx_rows(gate_up, m, act == QDM_F32 ? 4 : 2, act, 0)) return e;
+    if (int e = check_mx_rows(down, m, 4, act, 1)) return e;
     const int32_t d = gate_up->k, ffn = gate_up->n;
     if (!workspace || workspace_bytes < qdm_mlp_rmsnorm_workspace_bytes(m, d, ffn, act)) return QDM_ERR_WORKSPACE;
     if (s_out == out) return QDM_ERR_INVALID_ARG;

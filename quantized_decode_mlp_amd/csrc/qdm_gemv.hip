@@ -230,13 +230,12 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
         if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);   // MX: streaming kernel only
         return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s, n_out);
     }
-    if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);
-    // 2..16 rows on the matrix cores.  Gate/up with 8/4-bit weights and 16-bit
-    // activations, down with 8/4-bit weights and a 16-bit output: the
+    // 2..16 rows on the matrix cores.  Gate/up with 8/4-bit or MX weights and
+    // 16-bit activations, down with such weights and a 16-bit output: the
     // weight-streaming kernels (down split along K).  Otherwise the tile-per-block
     // kernel: gate/up with bf16 activations (exact MMA operands), down with any
     // 16-bit output (h enters as a bf16 hi/lo split, ~16 significant bits, so
-    // fp32 outputs stay on the vector path)
+    // fp32 outputs stay on the vector path); MX weights take only the former.
     if constexpr (GU) {
         if (mma_stream_gate_up_supported(w, m, XDT))
             return launch_gate_up_mma_stream(x, m, XDT, w, static_cast<float*>(out), s);
@@ -244,6 +243,7 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
         if (mma_stream_down_supported(w, m, ODT))
             return launch_down_mma_stream(static_cast<const float*>(x), r, m, ODT, w, out, s);
     }
+    if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);
     if (mma_rows_supported(w, m)) {
         if constexpr (GU) {
             if (XDT == DT_BF16) return launch_gate_up_mma(x, m, w, static_cast<float*>(out), s);

@@ -11,6 +11,7 @@
 
 #include <type_traits>
 
+#include "qdm.h"
 #include "qdm_device.h"
 
 namespace qdm {
@@ -118,6 +119,53 @@ struct StepCodes<4, DT_BF16> : StepWords<4> {
     }
 };
 
+// MX block-scaled elements (E4M3 bytes, E2M1 nibbles low first) as exact
+// operands in the MMA's type: the hardware converts a pair per instruction
+// (E4M3 bytes 0,1 / 2,3 of a dword; E2M1 nibbles of one byte), keeping k
+// order, so the staged activations stay in natural order.  No offset; the
+// block scale arrives through the (scale, bias) pair as (2^(e - 127), 0).
+template <int XDT>
+__device__ __forceinline__ uint32_t mx8_pair(uint32_t w, bool hi) {
+    if constexpr (XDT == DT_BF16) {
+        return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    } else {
+        return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    }
+}
+
+template <int XDT, int B>
+__device__ __forceinline__ uint32_t mx4_pair(uint32_t w) {
+    if constexpr (XDT == DT_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
+}
+
+template <int XDT>
+struct StepCodes<QDM_MXFP8, XDT> : StepWords<8> {
+    static constexpr float kOff = 0.f, kInvMul = 1.f;
+    __device__ __forceinline__ static u32x4 operand(raw w) {
+        return u32x4{mx8_pair<XDT>(w[0], false), mx8_pair<XDT>(w[0], true), mx8_pair<XDT>(w[1], false),
+                     mx8_pair<XDT>(w[1], true)};
+    }
+};
+
+template <int XDT>
+struct StepCodes<QDM_MXFP4, XDT> : StepWords<4> {
+    static constexpr float kOff = 0.f, kInvMul = 1.f;
+    __device__ __forceinline__ static u32x4 operand(raw w) {
+        return u32x4{mx4_pair<XDT, 0>(w), mx4_pair<XDT, 1>(w), mx4_pair<XDT, 2>(w), mx4_pair<XDT, 3>(w)};
+    }
+};
+
+constexpr bool mx_bits(int bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
+constexpr int code_width(int bits) { return bits & 0xff; }
+
+// An E8M0 code as its fp32 power of two (code 0: the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
+
 // k-block layout.  WIDE (groups of 64 or more): a k-block is KBK k, lane kq
 // holds the LK = KBK/4 consecutive k from LK*kq (one 16-byte load per row),
 // k-step t takes its codes 8t .. 8t+7; a block spanning NF > 1 groups runs
@@ -126,13 +174,14 @@ struct StepCodes<4, DT_BF16> : StepWords<4> {
 // 32t + 8kq .. +7 of step t (one load per step) and each step is one group.
 template <int BITS, int G>
 struct BlockLayout {
+    static constexpr int CB = code_width(BITS);   // bits per code
     static constexpr bool WIDE = G >= 64;
-    static constexpr int KBK = (BITS == 4 && WIDE) ? 128 : 64;
+    static constexpr int KBK = (CB == 4 && WIDE) ? 128 : 64;
     static constexpr int STEPS = KBK / 32;
     static constexpr int LK = KBK / 4;
     static constexpr int FG = WIDE ? (G < KBK ? G : KBK) : 32;   // fold chunk (k)
     static constexpr int NF = KBK / FG;                           // fold chunks per k-block
-    using Words = typename std::conditional<WIDE || BITS == 8, u32x4, u32x2>::type;
+    using Words = typename std::conditional<WIDE || CB == 8, u32x4, u32x2>::type;
 };
 
 __host__ __device__ constexpr size_t round16(size_t v) { return (v + 15) & ~static_cast<size_t>(15); }

@@ -80,7 +80,7 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
     const int t0 = tb * P + p;
     const int rounds = (ntiles - tb * P + GP - 1) / GP;   // same for the block
     if (rounds <= 0) return;   // uniform per block, before any barrier
-    const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;
+    const uint32_t rb = static_cast<uint32_t>(K) * L::CB / 8;
     const int ngroups = K / G;
 
     using Words = typename L::Words;
@@ -95,7 +95,16 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
 #pragma unroll
         for (int r = 0; r < NPL; ++r) {
             const int g = 8 * r + 2 * kq;
-            if (g < gw) pw[r] = *reinterpret_cast<const f32x4*>(sb + 2 * (row * ngroups + gbase + g));
+            if (g < gw) {
+                if constexpr (mx_bits(BITS)) {
+                    // MX: the two blocks' E8M0 bytes as (scale, 0) pairs
+                    const uint8_t* e = reinterpret_cast<const uint8_t*>(sb) + row * ngroups + gbase + g;
+                    const uint32_t e0 = e[0], e1 = e[1];
+                    pw[r] = f32x4{e8m0_value(e0), 0.f, e8m0_value(e1), 0.f};
+                } else {
+                    pw[r] = *reinterpret_cast<const f32x4*>(sb + 2 * (row * ngroups + gbase + g));
+                }
+            }
         }
     };
     auto pair_of = [&](int gl) -> f32x2 {
@@ -114,13 +123,13 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
         const uint8_t* qrow = q + static_cast<size_t>(tile * kRows + li) * rb;
         const int kb0 = k0w + j * KBK;
         if constexpr (WIDE) {
-            c = *reinterpret_cast<const Words*>(qrow + static_cast<uint32_t>(kb0 + L::LK * kq) * BITS / 8);
+            c = *reinterpret_cast<const Words*>(qrow + static_cast<uint32_t>(kb0 + L::LK * kq) * L::CB / 8);
         } else {
 #pragma unroll
             for (int t = 0; t < STEPS; ++t)
                 SC::set_step(c, t,
                              *reinterpret_cast<const typename SC::raw*>(
-                                 qrow + static_cast<uint32_t>(kb0 + 32 * t + 8 * kq) * BITS / 8));
+                                 qrow + static_cast<uint32_t>(kb0 + 32 * t + 8 * kq) * L::CB / 8));
         }
     };
 
@@ -354,7 +363,10 @@ int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int 
     if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
         return static_cast<int>(hipErrorInvalidValue);
-    hipError_t e = launch(kern, dim3(ns * sp.tb), dim3(NT), lds, s, static_cast<const uint8_t*>(w.q), w.scale_bias, h,
+    // MX: the block scales take the scale/bias argument (the kernel reads bytes)
+    const float* sbp = mx_bits(BITS) ? reinterpret_cast<const float*>(w.block_scales) : w.scale_bias;
+    if (!sbp) return static_cast<int>(hipErrorInvalidValue);
+    hipError_t e = launch(kern, dim3(ns * sp.tb), dim3(NT), lds, s, static_cast<const uint8_t*>(w.q), sbp, h,
                           part, w.n, w.k, sp.kr, sp.tb, m);
     if (e != hipSuccess) return static_cast<int>(e);
     const int outs = m * w.n;
@@ -374,7 +386,12 @@ int run_down_g(const qdm_weight& w, const float* h, const void* r, void* out, in
 
 template <int ODT>
 int run_down_b(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* rc) {
-    return w.bits == 8 ? run_down_g<8, ODT>(w, h, r, out, m, s, rc) : run_down_g<4, ODT>(w, h, r, out, m, s, rc);
+    switch (w.bits) {
+        case 8: return run_down_g<8, ODT>(w, h, r, out, m, s, rc);
+        case QDM_MXFP8: return run_down<QDM_MXFP8, 32, ODT>(w, h, r, out, m, s, rc);
+        case QDM_MXFP4: return run_down<QDM_MXFP4, 32, ODT>(w, h, r, out, m, s, rc);
+        default: return run_down_g<4, ODT>(w, h, r, out, m, s, rc);
+    }
 }
 
 template <int BITS, int G>
@@ -387,10 +404,12 @@ bool split_exists(int m, int n, int k) {
 
 bool mma_stream_down_supported(const qdm_weight& w, int m, int act) {
     if (m < 2 || m > kRows) return false;
-    if (w.bits != 8 && w.bits != 4) return false;
+    if (w.bits != 8 && w.bits != 4 && !mx_bits(w.bits)) return false;
     if (w.group != 32 && w.group != 64 && w.group != 128) return false;
     if (act != DT_BF16 && act != DT_F16) return false;   // h enters at ~16 bits: 16-bit outputs only
     if (w.n % kRows != 0) return false;
+    if (w.bits == QDM_MXFP8) return w.group == 32 && split_exists<QDM_MXFP8, 32>(m, w.n, w.k);
+    if (w.bits == QDM_MXFP4) return w.group == 32 && split_exists<QDM_MXFP4, 32>(m, w.n, w.k);
     if (w.bits == 4)
         return w.group == 32 ? split_exists<4, 32>(m, w.n, w.k)
              : w.group == 64 ? split_exists<4, 64>(m, w.n, w.k) : split_exists<4, 128>(m, w.n, w.k);

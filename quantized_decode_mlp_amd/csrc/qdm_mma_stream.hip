@@ -92,7 +92,7 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
     const int t0 = static_cast<int>(blockIdx.x) * P + p;
     const int rounds = (ntiles - static_cast<int>(blockIdx.x) * P + GP - 1) / GP;   // same for the block
     if (rounds <= 0) return;   // uniform per block, before any barrier
-    const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;
+    const uint32_t rb = static_cast<uint32_t>(K) * L::CB / 8;
     const int ngroups = K / G;
 
     // activation pieces (16 bytes, 8 values) ahead of the first weights
@@ -130,7 +130,16 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
 #pragma unroll
             for (int r = 0; r < NPL; ++r) {
                 const int g = 8 * r + 2 * kq;
-                if (g < gw) pw[v][r] = *reinterpret_cast<const f32x4*>(sb + 2 * (row * ngroups + gbase + g));
+                if (g < gw) {
+                    if constexpr (mx_bits(BITS)) {
+                        // MX: the two blocks' E8M0 bytes as (scale, 0) pairs
+                        const uint8_t* e = reinterpret_cast<const uint8_t*>(sb) + row * ngroups + gbase + g;
+                        const uint32_t e0 = e[0], e1 = e[1];
+                        pw[v][r] = f32x4{e8m0_value(e0), 0.f, e8m0_value(e1), 0.f};
+                    } else {
+                        pw[v][r] = *reinterpret_cast<const f32x4*>(sb + 2 * (row * ngroups + gbase + g));
+                    }
+                }
             }
         }
     };
@@ -156,12 +165,12 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
             const uint8_t* qrow = q + static_cast<size_t>(row) * rb;
             if constexpr (WIDE) {
                 const uint32_t k0 = static_cast<uint32_t>(kb * KBK + L::LK * kq);
-                s.c[v] = *reinterpret_cast<const Words*>(qrow + k0 * BITS / 8);
+                s.c[v] = *reinterpret_cast<const Words*>(qrow + k0 * L::CB / 8);
             } else {
 #pragma unroll
                 for (int t = 0; t < STEPS; ++t) {
                     const uint32_t k0 = static_cast<uint32_t>(kb * KBK + 32 * t + 8 * kq);
-                    SC::set_step(s.c[v], t, *reinterpret_cast<const typename SC::raw*>(qrow + k0 * BITS / 8));
+                    SC::set_step(s.c[v], t, *reinterpret_cast<const typename SC::raw*>(qrow + k0 * L::CB / 8));
                 }
             }
         }
@@ -387,8 +396,11 @@ int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t
     const int ntiles = w.n / kRows;
     const int need = (ntiles + kP - 1) / kP;
     const int blocks = need < res ? need : res;
-    return static_cast<int>(launch(kern, dim3(blocks), dim3(NT), lds, s, static_cast<const uint8_t*>(w.q),
-                                   w.scale_bias, x, h, w.n, w.k, m, na));
+    // MX: the block scales take the scale/bias argument (the kernel reads bytes)
+    const float* sbp = mx_bits(BITS) ? reinterpret_cast<const float*>(w.block_scales) : w.scale_bias;
+    if (!sbp) return static_cast<int>(hipErrorInvalidValue);
+    return static_cast<int>(launch(kern, dim3(blocks), dim3(NT), lds, s, static_cast<const uint8_t*>(w.q), sbp, x, h,
+                                   w.n, w.k, m, na));
 }
 
 template <int BITS, int XDT, bool NORM>
@@ -402,15 +414,21 @@ int run_gate_up_g(const qdm_weight& w, const void* x, float* h, int m, hipStream
 
 template <int XDT, bool NORM>
 int run_gate_up_x(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s, const NormArgs& na) {
-    return w.bits == 8 ? run_gate_up_g<8, XDT, NORM>(w, x, h, m, s, na) : run_gate_up_g<4, XDT, NORM>(w, x, h, m, s, na);
+    switch (w.bits) {
+        case 8: return run_gate_up_g<8, XDT, NORM>(w, x, h, m, s, na);
+        case QDM_MXFP8: return run_gate_up<QDM_MXFP8, XDT, 32, NORM>(w, x, h, m, s, na);
+        case QDM_MXFP4: return run_gate_up<QDM_MXFP4, XDT, 32, NORM>(w, x, h, m, s, na);
+        default: return run_gate_up_g<4, XDT, NORM>(w, x, h, m, s, na);
+    }
 }
 
 }  // namespace
 
 bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
     if (m < 2 || m > kRows) return false;
-    if (w.bits != 8 && w.bits != 4) return false;
+    if (w.bits != 8 && w.bits != 4 && !mx_bits(w.bits)) return false;
     if (w.group != 32 && w.group != 64 && w.group != 128) return false;
+    if (mx_bits(w.bits) && w.group != 32) return false;
     if (act != DT_BF16 && act != DT_F16) return false;
     const int kbk = (w.bits == 4 && w.group >= 64) ? 128 : 64;
     if (w.n % kRows != 0 || w.k % (kbk * kS) != 0) return false;
@@ -419,7 +437,8 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
     const int npl = w.group == 32 ? pair_regs<32>() : pair_regs<64>();
     if (gw * w.group * kS != w.k || gw % 2 != 0 || gw > 8 * npl) return false;
     // staged rows, chunk sums and the combine buffer within one CU's LDS
-    const size_t dyn = w.bits == 4 ? (w.group == 32 ? gate_up_lds_bytes<4, 32>(m, w.k)
+    const size_t dyn = mx_bits(w.bits) ? gate_up_lds_bytes<QDM_MXFP8, 32>(m, w.k)
+                     : w.bits == 4 ? (w.group == 32 ? gate_up_lds_bytes<4, 32>(m, w.k)
                                       : w.group == 64 ? gate_up_lds_bytes<4, 64>(m, w.k)
                                                       : gate_up_lds_bytes<4, 128>(m, w.k))
                                    : (w.group == 32 ? gate_up_lds_bytes<8, 32>(m, w.k)

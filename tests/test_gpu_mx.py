@@ -4,7 +4,8 @@ weight-streaming kernel's hardware-decoded forms) through the C ABI.
 Bars: h within 1e-5 scaled error and y within 5e-3 (bf16 / f16) or 1e-5
 (fp32) of the fp64 oracle on the oracle's own MX dequantization of the same
 fp32 draws; the chained call bitwise equal to add + RMSNorm then the MLP;
-projections on sampled rows at vocabulary size; several rows rejected."""
+projections on sampled rows at vocabulary size; 2..16 rows on the
+matrix-core kernels; several-row projections rejected."""
 import numpy as np
 import pytest
 
@@ -138,12 +139,57 @@ def test_mx_projection_with_bias(name):
     assert oracle.scaled_error(from_device(y), ref) <= TOL["bf16"]
 
 
-def test_mx_several_rows_rejected():
+@pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("m", [2, 4, 16])
+def test_mx_rows(m, act, name):
+    """Several rows on the matrix-core kernels: elements converted to exact
+    operands, the block scale folded per 32-wide chunk."""
+    print(f"[mx] rows m={m} act={act} {name}", flush=True)
+    d, ffn = 1024, 1536
+    g32 = W.generic_weights((m, 1), ffn, d, 0.05)
+    u32 = W.generic_weights((m, 2), ffn, d, 0.05)
+    d32 = W.generic_weights((m, 3), d, ffn, 0.05)
+    deq, pw = _mx_case(g32, u32, d32, name)
+    x = W.generic_act((m, 4), (m, d), act)
+    r = W.generic_act((m, 5), (m, d), act)
+    _check_mlp(deq, pw, x, r, act)
+
+
+@pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
+def test_mx_rows_llama3_8b_shape(name):
+    wl = W.WORKLOADS[5]
+    print(f"[mx] workload 5 m=4 {name}", flush=True)
+    deq, pw = _mx_case(*W.weights_f32(wl, 0), name)
+    x, r = W.activations(wl, 4)
+    _check_mlp(deq, pw, x, r, wl.act)
+
+
+def test_mx_rows_chain():
+    """The chain at 4 rows with MX weights: bitwise equal to the three launches."""
     qdm = _qdm()
-    d, ffn = 256, 512
-    _, (gu, dn) = _mx_case(W.generic_weights((1,), ffn, d), W.generic_weights((2,), ffn, d),
-                           W.generic_weights((3,), d, ffn), "mxfp8")
-    x = to_device(W.generic_act((1,), (4, d), "bf16"))
+    print("[mx] rows chain m=4 mxfp4", flush=True)
+    m, d, ffn = 4, 1024, 1536
+    _, (gu, dn) = _mx_case(W.generic_weights((9, 1), ffn, d), W.generic_weights((9, 2), ffn, d),
+                           W.generic_weights((9, 3), d, ffn), "mxfp4")
+    a = to_device(W.generic_act((9, 4), (m, d), "bf16"))
+    b = to_device(W.generic_act((9, 5), (m, d), "bf16"))
+    w = to_device(W.to_storage(np.random.default_rng(9).uniform(0.5, 1.5, d).astype(np.float32), "bf16"))
+    s = torch.empty_like(a)
+    y = qdm.mlp_decode_rmsnorm(a, b, w, 1e-5, gu, dn, s_out=s)
+    s_u, n_u = qdm.add_rmsnorm(a, b, w, 1e-5)
+    y_u = qdm.mlp_decode(n_u, s_u, gu, dn)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_u) and torch.equal(s, s_u)
+
+
+def test_mx_rows_projection_rejected():
+    """Projections with MX weights take one row only."""
+    qdm = _qdm()
+    n, k = 256, 512
+    qq, e = qdm.quantize_mx(W.generic_weights((1,), n, k), qdm.QDM_MXFP8)
+    pw = qdm.Weight.from_host(n, k, qdm.QDM_MXFP8, 32, qq, None, block_scales=e)
+    x = to_device(W.generic_act((1,), (4, k), "bf16"))
     with pytest.raises(qdm.QdmError) as ei:
-        qdm.mlp_decode(x, x.clone(), gu, dn)
+        qdm.gemv_linear(x, pw)
     assert ei.value.status == qdm.QDM_ERR_UNSUPPORTED
