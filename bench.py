@@ -255,8 +255,9 @@ def group_sweep(samples, dev):
 
 
 def mx_configs(samples, dev):
-    """The Qwen3-8B-shaped one-row MLP with MXFP8 and MXFP4 block-scaled weights, over
-    address-distinct copies of at least 2 GiB."""
+    """The Qwen3-8B-shaped one-row MLP with MXFP8 and MXFP4 block-scaled weights, and the
+    Llama-3-8B-shaped MLP in MXFP4 at 1, 4 and 16 rows, over address-distinct copies of at
+    least 2 GiB."""
     import torch
     import quantized_decode_mlp_amd as qdm
     res = {}
@@ -282,6 +283,36 @@ def mx_configs(samples, dev):
         _log(f"{name}: {med:.2f} us/layer")
         del sets
         torch.cuda.empty_cache()
+    del g32, u32, d32
+    # the Llama-3-8B-shaped layer in MXFP4 at 1, 4 and 16 rows
+    wl = W.WORKLOADS[5]
+    g32, u32, d32 = W.weights_f32(wl, 0)
+    fmt = qdm.QDM_MXFP4
+    q, e = qdm.quantize_mx_gate_up(g32, u32, fmt)
+    dq, de = qdm.quantize_mx(d32, fmt)
+    del g32, u32, d32
+    nbytes = q.nbytes + e.nbytes + dq.nbytes + de.nbytes
+    copies = int(-(-(2 << 30) // nbytes))
+    sets = [(qdm.Weight.from_host(wl.ffn, wl.d, fmt, 32, q, None, block_scales=e),
+             qdm.Weight.from_host(wl.d, wl.ffn, fmt, 32, dq, None, block_scales=de)) for _ in range(copies)]
+    for m in wl.rows:
+        x, r = W.activations(wl, m)
+        xd, rd = dev(x), dev(r)
+        ws = torch.empty(qdm.mlp_workspace_bytes(m, wl.ffn), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(rd)
+        try:
+            t = graph_samples(lambda i: qdm.mlp_decode(xd, rd, *sets[i], workspace=ws, out=out), copies, samples)
+        except qdm.QdmError as err:
+            res[f"llama3_8b_mxfp4_m{m}"] = {"unsupported": str(err)}
+            continue
+        med = float(np.median(t))
+        res[f"llama3_8b_mxfp4_m{m}"] = {"us_per_layer": pcts(t), "weight_bytes": int(nbytes),
+                                        "weight_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                        "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                                        "copies": copies}
+        _log(f"llama3_8b mxfp4 m={m}: {med:.2f} us/layer")
+    del sets
+    torch.cuda.empty_cache()
     return res
 
 

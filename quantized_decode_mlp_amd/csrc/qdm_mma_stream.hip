@@ -43,11 +43,12 @@
 namespace qdm {
 namespace {
 
-// Dynamic LDS of the gate/up kernel: staged rows, then the fold-chunk sums.
+// Dynamic LDS of the gate/up kernel: staged rows, then the fold-chunk sums
+// (MX weights have no bias term and keep none).
 template <int BITS, int G>
 size_t gate_up_lds_bytes(int m, int k) {
     return round16(static_cast<size_t>(m) * (k + kPad) * 2) +
-           static_cast<size_t>(k / BlockLayout<BITS, G>::FG) * kRows * 4;
+           (mx_bits(BITS) ? 0 : static_cast<size_t>(k / BlockLayout<BITS, G>::FG) * kRows * 4);
 }
 
 // Inputs of the decode-chain form (NORM): the staged rows are
@@ -198,21 +199,25 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
                     o[i] = __builtin_amdgcn_perm(v[2 + (i >> 1)], v[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
             }
             *reinterpret_cast<u32x4*>(xs + m * ldx + c * 8) = o;
+            if constexpr (!mx_bits(BITS)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // the word goes through a scalar: __builtin_bit_cast of a vector
-                // element expression reinterprets the vector's first element
-                const uint32_t word = v[i];
-                if constexpr (XDT == DT_BF16)
-                    sum += __uint_as_float(word << 16) + __uint_as_float(word & 0xffff0000u);
-                else
-                    sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), __builtin_bit_cast(h16x2, 0x3c003c00u),
-                                                 sum, false);
+                for (int i = 0; i < 4; ++i) {
+                    // the word goes through a scalar: __builtin_bit_cast of a vector
+                    // element expression reinterprets the vector's first element
+                    const uint32_t word = v[i];
+                    if constexpr (XDT == DT_BF16)
+                        sum += __uint_as_float(word << 16) + __uint_as_float(word & 0xffff0000u);
+                    else
+                        sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word),
+                                                     __builtin_bit_cast(h16x2, 0x3c003c00u), sum, false);
+                }
             }
         }
+        if constexpr (!mx_bits(BITS)) {
 #pragma unroll
-        for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
-        if (u < npieces && c % CPF == 0) xsum[(c / CPF) * kRows + m] = sum;
+            for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
+            if (u < npieces && c % CPF == 0) xsum[(c / CPF) * kRows + m] = sum;
+        }
     };
     if constexpr (NORM) {
         // The decode chain's RMSNorm per row, recomputed by every block: s =
@@ -280,9 +285,11 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
             stage_piece(u, u < npieces ? xg[u] : u32x4{0u, 0u, 0u, 0u});
         }
     }
-    for (int u = static_cast<int>(threadIdx.x); u < (K / FG) * (kRows - m_rows); u += NT) {
-        const int ch = u / (kRows - m_rows), m = m_rows + (u - ch * (kRows - m_rows));
-        xsum[ch * kRows + m] = 0.f;
+    if constexpr (!mx_bits(BITS)) {
+        for (int u = static_cast<int>(threadIdx.x); u < (K / FG) * (kRows - m_rows); u += NT) {
+            const int ch = u / (kRows - m_rows), m = m_rows + (u - ch * (kRows - m_rows));
+            xsum[ch * kRows + m] = 0.f;
+        }
     }
     __syncthreads();
 
@@ -320,14 +327,24 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         }
 #pragma unroll
         for (int fc = 0; fc < NF; ++fc) {
-            const f32x4 xc = *reinterpret_cast<const f32x4*>(xsum + ((kb * KBK) / FG + fc) * kRows + 4 * kq);
+            if constexpr (mx_bits(BITS)) {
+                // MX: the block scale times the partial tile (no bias, no offset)
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                const f32x2 pv = pair_of(v, (j * KBK + fc * FG) / G);
-                // scale * sum c x + bias * X with sum c x = inv * (P - off * X)
-                const float se = pv.x * SC::kInvMul, be = fmaf(-SC::kOff, se, pv.y);
+                for (int v = 0; v < 2; ++v) {
+                    const float se = pair_of(v, (j * KBK + fc * FG) / G).x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[v][e] = fmaf(se, pt[fc][v][e], fmaf(be, xc[e], acc[v][e]));
+                    for (int e = 0; e < 4; ++e) acc[v][e] = fmaf(se, pt[fc][v][e], acc[v][e]);
+                }
+            } else {
+                const f32x4 xc = *reinterpret_cast<const f32x4*>(xsum + ((kb * KBK) / FG + fc) * kRows + 4 * kq);
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const f32x2 pv = pair_of(v, (j * KBK + fc * FG) / G);
+                    // scale * sum c x + bias * X with sum c x = inv * (P - off * X)
+                    const float se = pv.x * SC::kInvMul, be = fmaf(-SC::kOff, se, pv.y);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[v][e] = fmaf(se, pt[fc][v][e], fmaf(be, xc[e], acc[v][e]));
+                }
             }
         }
     };

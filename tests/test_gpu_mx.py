@@ -156,12 +156,13 @@ def test_mx_rows(m, act, name):
     _check_mlp(deq, pw, x, r, act)
 
 
+@pytest.mark.parametrize("m", [4, 16])
 @pytest.mark.parametrize("name", ["mxfp8", "mxfp4"])
-def test_mx_rows_llama3_8b_shape(name):
+def test_mx_rows_llama3_8b_shape(name, m):
     wl = W.WORKLOADS[5]
-    print(f"[mx] workload 5 m=4 {name}", flush=True)
+    print(f"[mx] workload 5 m={m} {name}", flush=True)
     deq, pw = _mx_case(*W.weights_f32(wl, 0), name)
-    x, r = W.activations(wl, 4)
+    x, r = W.activations(wl, m)
     _check_mlp(deq, pw, x, r, wl.act)
 
 
