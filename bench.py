@@ -184,7 +184,7 @@ def other_configs(samples, only=None):
         copies = int(-(-(2 << 30) // wl.weight_bytes))
         sets = [(qdm.Weight.from_host(wl.ffn, wl.d, wl.bits, wl.group, q, sb),
                  qdm.Weight.from_host(wl.d, wl.ffn, wl.bits, wl.group, dq, dsb)) for _ in range(copies)]
-        for m in ((only[1],) if only else (wl.rows if wi == 5 else (1,))):
+        for m in ((only[1],) if only else (wl.rows + (128,) if wi == 5 else (1,))):
             x, r = W.activations(wl, m)
             xd, rd = dev(x), dev(r)
             ws = torch.empty(qdm.mlp_workspace_bytes(m, wl.ffn), dtype=torch.uint8, device="cuda")
@@ -196,6 +196,7 @@ def other_configs(samples, only=None):
             if m > 1:
                 flops = 2 * m * 3 * wl.d * wl.ffn
                 rec["mfma_util_bf16"] = round(flops / (med * 1e-6) / 2.5e15, 5)
+                rec["tflops"] = round(flops / (med * 1e-6) / 1e12, 2)
             res[f"workload{wi}_m{m}"] = rec
             _log(f"workload {wi} m={m}: {med:.2f} us/layer")
         del sets

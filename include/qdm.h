@@ -190,7 +190,9 @@ int qdm_pack_dense_gate_up(const uint16_t* gate_bf16, const uint16_t* up_bf16,
  * Supported combinations (anything else returns QDM_ERR_UNSUPPORTED):
  *   act     QDM_F32, QDM_BF16 or QDM_F16: the dtype of x, r and out.
  *   weights bits 8 or 4 with group 32/64/128, or bits 16 (dense bf16).
- *   m       1..16 rows.
+ *   m       1..4096 rows.  Up to 16 rows run in one pass of the kernels; more
+ *           rows run as passes of 16 (each pass streams the weights again:
+ *           a functional form of multi-row prefill, not a tiled GEMM).
  *   k       a multiple of 16 (bits 8), 32 (bits 4) or 8 (bits 16).
  * Device pointers x, r, out, h, s_out, n_out, a, b, w must be 16-byte aligned. */
 

@@ -1,6 +1,7 @@
 // C-ABI entry points of the device path: argument validation, then dispatch to
 // the HIP launchers.  Every check runs before anything is launched, so a
 // rejected call writes nothing.  Host C++ only (no HIP headers needed here).
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -9,7 +10,8 @@
 
 namespace {
 
-constexpr int kMaxRows = 16;
+constexpr int kMaxRows = 4096;   // rows per call
+constexpr int kPassRows = 16;    // rows per kernel pass (the few-row kernels' matrix tile)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -43,20 +45,63 @@ int hip_status(int e) { return e == 0 ? QDM_OK : QDM_ERR_HIP; }
 
 bool is_mx(int32_t bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
 
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t act_bytes(int dt) { return dt == QDM_F32 ? 4 : 2; }
+
 // MX weights: one row on the weight-streaming kernel (x of xb bytes); 2..16
 // rows of a gate/up (kind 0) or down (kind 1) projection on the matrix-core
 // streaming kernels (16-bit activations / outputs); nothing else.
-int check_mx_rows(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
-    if (!is_mx(w->bits)) return QDM_OK;
+int check_mx_pass(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
     if (m == 1) return qdm::stream_supported(*w, xb) ? QDM_OK : QDM_ERR_UNSUPPORTED;
     if (kind == 0) return qdm::mma_stream_gate_up_supported(*w, m, act) ? QDM_OK : QDM_ERR_UNSUPPORTED;
     if (kind == 1) return qdm::mma_stream_down_supported(*w, m, act) ? QDM_OK : QDM_ERR_UNSUPPORTED;
     return QDM_ERR_UNSUPPORTED;
 }
 
-size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+// (rows run in passes of at most kPassRows: the full passes and the remainder are checked)
+int check_mx_rows(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
+    if (!is_mx(w->bits)) return QDM_OK;
+    if (m > kPassRows)
+        if (int e = check_mx_pass(w, kPassRows, xb, act, kind)) return e;
+    const int32_t rem = m % kPassRows;
+    return check_mx_pass(w, m <= kPassRows ? m : (rem ? rem : kPassRows), xb, act, kind);
+}
 
-size_t act_bytes(int dt) { return dt == QDM_F32 ? 4 : 2; }
+// The device calls over row passes of at most kPassRows rows (each pass streams the weights).
+int gate_up_passes(const void* x, int32_t m, int act, const qdm_weight& gu, float* h, void* stream) {
+    const size_t xe = act_bytes(act);
+    for (int32_t m0 = 0; m0 < m; m0 += kPassRows) {
+        const int32_t mr = std::min(kPassRows, m - m0);
+        if (int e = qdm::launch_gate_up_swiglu(static_cast<const char*>(x) + static_cast<size_t>(m0) * gu.k * xe, mr,
+                                               act, gu, h + static_cast<size_t>(m0) * gu.n, stream))
+            return e;
+    }
+    return 0;
+}
+
+int down_passes(const float* h, const void* r, int32_t m, int act, const qdm_weight& dn, void* out, void* stream) {
+    const size_t oe = act_bytes(act);
+    for (int32_t m0 = 0; m0 < m; m0 += kPassRows) {
+        const int32_t mr = std::min(kPassRows, m - m0);
+        const size_t ro = static_cast<size_t>(m0) * dn.n * oe;
+        if (int e = qdm::launch_down_residual(h + static_cast<size_t>(m0) * dn.k, static_cast<const char*>(r) + ro, mr,
+                                              act, dn, static_cast<char*>(out) + ro, stream))
+            return e;
+    }
+    return 0;
+}
+
+int linear_passes(const void* x, int32_t m, int act, const qdm_weight& w, const void* bias, void* out, void* stream) {
+    const size_t xe = act_bytes(act);
+    for (int32_t m0 = 0; m0 < m; m0 += kPassRows) {
+        const int32_t mr = std::min(kPassRows, m - m0);
+        if (int e = qdm::launch_linear(static_cast<const char*>(x) + static_cast<size_t>(m0) * w.k * xe, mr, act, w,
+                                       bias, static_cast<char*>(out) + static_cast<size_t>(m0) * w.n * xe, stream))
+            return e;
+    }
+    return 0;
+}
 
 }  // namespace
 
@@ -76,7 +121,7 @@ int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act, const qdm_w
     if (int e = check_weight(gate_up)) return e;
     if (int e = check_mx_rows(gate_up, m, act == QDM_F32 ? 4 : 2, act, 0)) return e;
     if (!aligned(x, 16) || !aligned(h_out, 16)) return QDM_ERR_ALIGNMENT;
-    return hip_status(qdm::launch_gate_up_swiglu(x, m, act, *gate_up, h_out, stream));
+    return hip_status(gate_up_passes(x, m, act, *gate_up, h_out, stream));
 }
 
 int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype act,
@@ -88,7 +133,7 @@ int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype a
     if (int e = check_weight(down)) return e;
     if (int e = check_mx_rows(down, m, 4, act, 1)) return e;
     if (!aligned(h, 16) || !aligned(r, 16) || !aligned(out, 16)) return QDM_ERR_ALIGNMENT;
-    return hip_status(qdm::launch_down_residual(h, r, m, act, *down, out, stream));
+    return hip_status(down_passes(h, r, m, act, *down, out, stream));
 }
 
 int qdm_gemv_linear(const void* x, int32_t m, qdm_dtype act, const qdm_weight* w, const void* bias, void* out,
@@ -100,7 +145,7 @@ int qdm_gemv_linear(const void* x, int32_t m, qdm_dtype act, const qdm_weight* w
     if (int e = check_weight(w)) return e;
     if (int e = check_mx_rows(w, m, act == QDM_F32 ? 4 : 2, act, 2)) return e;
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(bias, 16)) return QDM_ERR_ALIGNMENT;
-    return hip_status(qdm::launch_linear(x, m, act, *w, bias, out, stream));
+    return hip_status(linear_passes(x, m, act, *w, bias, out, stream));
 }
 
 int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
@@ -120,8 +165,8 @@ int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
     if (!aligned(x, 16) || !aligned(r, 16) || !aligned(out, 16) || !aligned(workspace, 16))
         return QDM_ERR_ALIGNMENT;
     float* h = static_cast<float*>(workspace);
-    if (int e = qdm::launch_gate_up_swiglu(x, m, act, *gate_up, h, stream)) return hip_status(e);
-    return hip_status(qdm::launch_down_residual(h, r, m, act, *down, out, stream));
+    if (int e = gate_up_passes(x, m, act, *gate_up, h, stream)) return hip_status(e);
+    return hip_status(down_passes(h, r, m, act, *down, out, stream));
 }
 
 size_t qdm_mlp_rmsnorm_workspace_bytes(int32_t m, int32_t d, int32_t ffn, qdm_dtype act) {
@@ -172,8 +217,8 @@ int qdm_mlp_decode_rmsnorm(const void* a, const void* b, const void* norm_w, flo
     void* n_buf = base + hb;
     void* s_buf = s_out ? s_out : static_cast<void*>(base + hb + vb);
     if (int e = qdm::launch_add_rmsnorm(a, b, norm_w, m, d, eps, act, s_buf, n_buf, stream)) return hip_status(e);
-    if (int e = qdm::launch_gate_up_swiglu(n_buf, m, act, *gate_up, h, stream)) return hip_status(e);
-    return hip_status(qdm::launch_down_residual(h, s_buf, m, act, *down, out, stream));
+    if (int e = gate_up_passes(n_buf, m, act, *gate_up, h, stream)) return hip_status(e);
+    return hip_status(down_passes(h, s_buf, m, act, *down, out, stream));
 }
 
 int qdm_add_rmsnorm(const void* a, const void* b, const void* w, int32_t rows, int32_t n,

@@ -73,7 +73,7 @@ def _gu(x=FAKE, m=1, act=q.QDM_BF16, w=None, h=FAKE):
     (dict(x=None), q.QDM_ERR_INVALID_ARG),
     (dict(h=None), q.QDM_ERR_INVALID_ARG),
     (dict(m=0), q.QDM_ERR_INVALID_ARG),
-    (dict(m=17), q.QDM_ERR_UNSUPPORTED),
+    (dict(m=4097), q.QDM_ERR_UNSUPPORTED),
     (dict(act=7), q.QDM_ERR_INVALID_ARG),
     (dict(w=_w(group=16)), q.QDM_ERR_UNSUPPORTED),
     (dict(w=_w(k=96, group=64)), q.QDM_ERR_INVALID_ARG),
@@ -155,7 +155,7 @@ def test_linear_rejects():
     assert f(out=X) == q.QDM_ERR_INVALID_ARG                          # out aliases x
     assert f(out=BIAS) == q.QDM_ERR_INVALID_ARG                       # out aliases bias
     assert f(m=0) == q.QDM_ERR_INVALID_ARG
-    assert f(m=17) == q.QDM_ERR_UNSUPPORTED
+    assert f(m=4097) == q.QDM_ERR_UNSUPPORTED
     assert f(dt=5) == q.QDM_ERR_INVALID_ARG
     assert f(w=_w(n=300, k=256, bits=2)) == q.QDM_ERR_UNSUPPORTED
     assert f(w=_w(n=300, k=250, group=32)) == q.QDM_ERR_INVALID_ARG
@@ -186,7 +186,7 @@ def test_chain_rejects():
     assert f(eps=float("nan")) == q.QDM_ERR_INVALID_ARG
     assert f(eps=-1.0) == q.QDM_ERR_INVALID_ARG
     assert f(dt=7) == q.QDM_ERR_INVALID_ARG
-    assert f(m=17) == q.QDM_ERR_UNSUPPORTED
+    assert f(m=4097) == q.QDM_ERR_UNSUPPORTED
     assert f(dn=_w(n=256, k=1024)) == q.QDM_ERR_INVALID_ARG          # ffn mismatch
     assert f(dn=_w(n=256, k=512, bits=4)) == q.QDM_ERR_UNSUPPORTED   # mixed formats
     assert f(b=ODD) == q.QDM_ERR_ALIGNMENT

@@ -1,0 +1,112 @@
+"""GPU parity with more than 16 rows (the functional multi-row prefill form:
+passes of 16 rows through the few-row kernels) through the C ABI.
+
+Bars as for the MLP: h within 1e-5 scaled error, y within 5e-3 (bf16) of the
+fp64 oracle; the chain bitwise equal to add + RMSNorm then the MLP."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_cases import H_TOL, TOL, from_device, generic_case, to_device, workload_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a GPU")
+    import quantized_decode_mlp_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def _qdm():
+    import quantized_decode_mlp_amd as qdm
+    return qdm
+
+
+def _check(ow, pw, x, r, act):
+    qdm = _qdm()
+    gu, dn = pw
+    xd, rd = to_device(x), to_device(r)
+    h = qdm.gemv_gate_up_swiglu(xd, gu)
+    y = qdm.mlp_decode(xd, rd, gu, dn)
+    torch.cuda.synchronize()
+    h_ref, y_ref = oracle.mlp_decode(x.values, r.values, ow.wg, ow.wu, ow.wd)
+    eh = oracle.scaled_error(from_device(h), h_ref)
+    ey = oracle.scaled_error(from_device(y), y_ref)
+    print(f"  h err {eh:.3e}  y err {ey:.3e}", flush=True)
+    assert eh <= H_TOL, eh
+    assert ey <= TOL[act], ey
+
+
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (16, 0)])
+@pytest.mark.parametrize("m", [17, 40, 64])
+def test_prefill_rows(m, bits, group):
+    print(f"[prefill] m={m} bits={bits} group={group}", flush=True)
+    d, ffn = 1024, 1536
+    ow, pw = generic_case((m, bits, 7), d, ffn, bits, group)
+    x = W.generic_act((m, 1), (m, d), "bf16")
+    r = W.generic_act((m, 2), (m, d), "bf16")
+    _check(ow, pw, x, r, "bf16")
+
+
+def test_prefill_llama3_8b_shape():
+    wl = W.WORKLOADS[5]
+    print("[prefill] workload 5 m=128", flush=True)
+    ow, pw = workload_case(5)
+    x, r = W.activations(wl, 128)
+    _check(ow, pw, x, r, wl.act)
+
+
+def test_prefill_projection_with_bias():
+    qdm = _qdm()
+    m, n, k = 33, 1003, 1024
+    w32 = W.generic_weights((m, n), n, k, 0.05)
+    q, sb = qdm.quantize_pack_rows(w32, 8, 64)
+    pw = qdm.Weight.from_host(n, k, 8, 64, q, sb)
+    c, s, b = oracle.quantize_affine(w32, 8, 64)
+    x = W.generic_act((m, 3), (m, k), "bf16")
+    bias = W.generic_act((n, 4), (n,), "bf16", 0.1)
+    y = qdm.gemv_linear(to_device(x), pw, bias=to_device(bias))
+    torch.cuda.synchronize()
+    ref = oracle.linear(x.values, oracle.dequantize(c, s, b, 64), bias.values)
+    assert oracle.scaled_error(from_device(y), ref) <= TOL["bf16"]
+
+
+def test_prefill_chain():
+    qdm = _qdm()
+    m, d, ffn = 20, 1024, 1536
+    _, (gu, dn) = generic_case((m, 9), d, ffn, 4, 64)
+    a = to_device(W.generic_act((m, 5), (m, d), "bf16"))
+    b = to_device(W.generic_act((m, 6), (m, d), "bf16"))
+    w = to_device(W.to_storage(np.random.default_rng(m).uniform(0.5, 1.5, d).astype(np.float32), "bf16"))
+    s = torch.empty_like(a)
+    y = qdm.mlp_decode_rmsnorm(a, b, w, 1e-5, gu, dn, s_out=s)
+    s_u, n_u = qdm.add_rmsnorm(a, b, w, 1e-5)
+    y_u = qdm.mlp_decode(n_u, s_u, gu, dn)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_u) and torch.equal(s, s_u)
+
+
+def test_prefill_mx_rows():
+    qdm = _qdm()
+    m, d, ffn = 40, 1024, 1536
+    fmt = qdm.QDM_MXFP4
+    g32, u32 = W.generic_weights((m, 11), ffn, d), W.generic_weights((m, 12), ffn, d)
+    d32 = W.generic_weights((m, 13), d, ffn)
+    q, e = qdm.quantize_mx_gate_up(g32, u32, fmt)
+    gu = qdm.Weight.from_host(ffn, d, fmt, 32, q, None, block_scales=e)
+    dq, de = qdm.quantize_mx(d32, fmt)
+    dn = qdm.Weight.from_host(d, ffn, fmt, 32, dq, None, block_scales=de)
+    deq = [oracle.dequantize_mx(*oracle.quantize_mx(a, "mxfp4"), "mxfp4") for a in (g32, u32, d32)]
+    x = W.generic_act((m, 14), (m, d), "bf16")
+    r = W.generic_act((m, 15), (m, d), "bf16")
+    y = qdm.mlp_decode(to_device(x), to_device(r), gu, dn)
+    torch.cuda.synchronize()
+    _, y_ref = oracle.mlp_decode(x.values, r.values, *deq)
+    assert oracle.scaled_error(from_device(y), y_ref) <= TOL["bf16"]
