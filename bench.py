@@ -449,8 +449,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(multi-GPU sharding is a design note, not built)"}))
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 "
+                                   "(sharding across GPUs is designed, not built)"}))
         return 2
 
     import torch

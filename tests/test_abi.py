@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_gfx950_code_object_present():
-    # the offload bundle of this build names its target id
+    # the library's offload bundle names its target id
     data = open(q.LIB_PATH, "rb").read()
     assert b"amdgcn-amd-amdhsa--gfx950" in data
 
