@@ -10,6 +10,8 @@ What it computes (plain definitions, numpy, float64):
 * ``quantize_affine`` / ``dequantize`` -- affine group quantization along the
   input dim, groups of 32/64/128 (meTile docs, "MLX-LM Backend" page, the
   affine INT8 / 4-bit passages: per-group scales and biases, nibbles).
+* ``quantize_affine_bf16sb`` / ``dequantize_bf16sb`` -- the same format with
+  bf16 (scale, bias) pairs.
 * ``pack_*`` / ``unpack_*`` -- the packed byte layouts the GPU path reads.
 * ``gate_up_swiglu`` -- h = silu(W_gate x) * (W_up x) ("Compute-Graph Fusion"
   page, section "Automatic Gated Epilogues").
@@ -34,7 +36,8 @@ forms, textbook values, hand-derived fixtures under ``tests/golden/`` and a
 brute-force rational implementation on tiny inputs.  No function here is
 "parity unpinned".
 """
-from .quantize import quantize_affine, dequantize, dequantize_dense_bf16
+from .quantize import (quantize_affine, dequantize, dequantize_dense_bf16, quantize_affine_bf16sb,
+                       dequantize_bf16sb)
 from .pack import (pack_codes, unpack_codes, pack_scale_bias, unpack_scale_bias,
                    pack_gate_up, pack_gate_up_scale_bias, pack_dense_gate_up)
 from .mlp import silu, gate_up_swiglu, down_residual, mlp_decode
@@ -45,7 +48,7 @@ from .mx import quantize_mx, dequantize_mx, decode_element, decode_scale, pack_m
 from .compare import scaled_error
 
 __all__ = [
-    "quantize_affine", "dequantize", "dequantize_dense_bf16",
+    "quantize_affine", "dequantize", "dequantize_dense_bf16", "quantize_affine_bf16sb", "dequantize_bf16sb",
     "pack_codes", "unpack_codes", "pack_scale_bias", "unpack_scale_bias",
     "pack_gate_up", "pack_gate_up_scale_bias", "pack_dense_gate_up",
     "silu", "gate_up_swiglu", "down_residual", "mlp_decode",

@@ -74,3 +74,36 @@ def dequantize_dense_bf16(bits) -> np.ndarray:
     16 fraction bits are zero."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def quantize_affine_bf16sb(w, bits: int, group: int):
+    """The same affine format with its (scale, bias) stored as bf16 -- the
+    dtype MLX keeps them in for bf16 models ("MLX-LM Backend": affine
+    weights keep per-group scales and biases; their storage type is not
+    printed).  Reading used: scale and bias as in ``quantize_affine``, each
+    rounded once to bf16 (nearest-even), then every code chosen against the
+    rounded pair, q = clamp(rint((fp64(w) - fp64(bias_bf16)) / fp64(scale_bf16)),
+    0, 2^bits - 1) (all 0 when the rounded scale is 0), so that dequantization
+    with the stored pair is what the codes were chosen for.
+    Returns (codes uint8 [n, k], scale [n, k/g], bias [n, k/g]) with the
+    bf16 values in fp64."""
+    from .rmsnorm import round_to_dtype
+    _, scale32, bias32 = quantize_affine(w, bits, group)
+    n, k = np.asarray(w).shape
+    qmax = (1 << bits) - 1
+    scale = round_to_dtype(scale32.astype(np.float64), "bf16")
+    bias = round_to_dtype(bias32.astype(np.float64), "bf16")
+    live = scale != 0
+    wg = np.asarray(w, dtype=np.float32).reshape(n, k // group, group).astype(np.float64)
+    denom = np.where(live, scale, 1.0)[..., None]
+    q = np.clip(np.rint((wg - bias[..., None]) / denom), 0, qmax)
+    q = np.where(live[..., None], q, 0.0)
+    return q.astype(np.uint8).reshape(n, k), scale, bias
+
+
+def dequantize_bf16sb(codes, scale, bias, group: int) -> np.ndarray:
+    """w~ = scale * q + bias with the bf16 pair (given as fp64 values)."""
+    codes = np.asarray(codes)
+    s = np.repeat(np.asarray(scale, dtype=np.float64), group, axis=1)
+    b = np.repeat(np.asarray(bias, dtype=np.float64), group, axis=1)
+    return s * codes.astype(np.float64) + b
