@@ -205,6 +205,7 @@ def other_configs(samples, only=None):
         return res
     res.update(projection_configs(samples, dev))
     res["group_sweep"] = group_sweep(samples, dev)
+    res["bf16_scale_bias"] = sb16_configs(samples, dev)
     res.update(mx_configs(samples, dev))
     # add + RMSNorm (the row-a5 kernel) on the Llama-3.2-1B-shaped f16 row, and a launch floor
     wl = W.WORKLOADS[2]
@@ -314,6 +315,40 @@ def mx_configs(samples, dev):
         _log(f"llama3_8b mxfp4 m={m}: {med:.2f} us/layer")
     del sets
     torch.cuda.empty_cache()
+    return res
+
+
+def sb16_configs(samples, dev):
+    """Each quantized workload's MLP with its (scale, bias) pairs stored as bf16 (the
+    QDM_U8_SB16 / QDM_U4_SB16 formats), over address-distinct copies of at least 2 GiB."""
+    import torch
+    import quantized_decode_mlp_amd as qdm
+    res = {}
+    for wi in (2, 4, 5):
+        wl = W.WORKLOADS[wi]
+        g32, u32, d32 = W.weights_f32(wl, 0)
+        q, sb = qdm.quantize_pack_gate_up_sb16(g32, u32, wl.bits, wl.group)
+        dq, dsb = qdm.quantize_pack_rows_sb16(d32, wl.bits, wl.group)
+        del g32, u32, d32
+        fmt = qdm.QDM_U8_SB16 if wl.bits == 8 else qdm.QDM_U4_SB16
+        nbytes = q.nbytes + sb.nbytes + dq.nbytes + dsb.nbytes
+        copies = int(-(-(2 << 30) // nbytes))
+        sets = [(qdm.Weight.from_host(wl.ffn, wl.d, fmt, wl.group, q, sb),
+                 qdm.Weight.from_host(wl.d, wl.ffn, fmt, wl.group, dq, dsb)) for _ in range(copies)]
+        for m in ((1, 4, 16) if wi == 5 else (1,)):
+            x, r = W.activations(wl, m)
+            xd, rd = dev(x), dev(r)
+            ws = torch.empty(qdm.mlp_workspace_bytes(m, wl.ffn), dtype=torch.uint8, device="cuda")
+            out = torch.empty_like(rd)
+            t = graph_samples(lambda i: qdm.mlp_decode(xd, rd, *sets[i], workspace=ws, out=out), copies, samples)
+            med = float(np.median(t))
+            res[f"workload{wi}_m{m}"] = {"us_per_layer": pcts(t), "weight_bytes": int(nbytes),
+                                         "weight_GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                         "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                                         "copies": copies}
+            _log(f"bf16 pairs workload {wi} m={m}: {med:.2f} us/layer")
+        del sets
+        torch.cuda.empty_cache()
     return res
 
 

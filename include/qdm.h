@@ -36,6 +36,10 @@
  *   4  : affine 4-bit codes, two per byte, row-major [n][k/2]; byte i of a row
  *        holds code 2i in its low nibble and code 2i+1 in its high nibble;
  *   16 : dense bf16 weights [n][k] (no scale/bias; group = 0);
+ *   QDM_U8_SB16, QDM_U4_SB16 : the affine 8 / 4-bit formats with the
+ *        (scale, bias) pairs stored as bf16 (two uint16 per group,
+ *        [n][k/group][2], 4-byte aligned), the dtype MLX keeps them in for
+ *        bf16 models;
  *   QDM_MXFP8, QDM_MXFP4 : block-scaled weights ("MLX-LM Backend" page,
  *        section "Block-Scaled MLX Primitive": E8M0 block scales with E4M3 or
  *        E2M1 elements; read as the OCP Microscaling formats): blocks of 32
@@ -73,8 +77,8 @@ typedef enum qdm_status {
 
 typedef enum qdm_dtype { QDM_F32 = 0, QDM_F16 = 1, QDM_BF16 = 2 } qdm_dtype;
 
-/* Values of qdm_weight.bits besides 4, 8 and 16. */
-enum { QDM_MXFP4 = 0x104, QDM_MXFP8 = 0x108 };
+/* Values of qdm_weight.bits besides 4, 8 and 16 (the low byte is the code width). */
+enum { QDM_MXFP4 = 0x104, QDM_MXFP8 = 0x108, QDM_U4_SB16 = 0x204, QDM_U8_SB16 = 0x208 };
 
 /* A packed weight matrix in device memory, described once per weight set and
  * reused for every call (the pages bind prepared weights once into a warmed
@@ -86,9 +90,10 @@ enum { QDM_MXFP4 = 0x104, QDM_MXFP8 = 0x108 };
  *   group       32, 64 or 128 for bits 8/4 (k % group == 0); 0 for bits 16;
  *               32 for the MX formats.
  *   q           device, 16-byte aligned: packed codes or bf16 words.
- *   scale_bias  device, 8-byte aligned: fp32 pairs; NULL for bits 16 and MX.
+ *   scale_bias  device, 8-byte aligned: fp32 pairs (bf16 pairs, 4-byte aligned, for
+ *               the _SB16 formats); NULL for bits 16 and MX.
  *   block_scales device: E8M0 bytes [n][k/32] for MX; NULL otherwise.
- * MX weights are taken by the one-row calls (m = 1) whose projections run on
+ * MX and _SB16 weights are taken by the one-row calls (m = 1) whose projections run on
  * the weight-streaming kernel, and by the MLP calls with 2..16 rows and a
  * 16-bit act dtype whose projections run on the matrix-core streaming
  * kernels; anything else (qdm_gemv_linear with m > 1 among it) returns
@@ -162,6 +167,20 @@ int qdm_pack_gate_up(const uint8_t* gate_codes, const float* gate_scale, const f
                      const uint8_t* up_codes, const float* up_scale, const float* up_bias,
                      int32_t ffn, int32_t d, int32_t bits, int32_t group,
                      void* q_out, float* scale_bias_out);
+
+/* Affine quantize + pack with bf16 (scale, bias) pairs (the pages do not
+ * print the pairs' storage type; MLX keeps them in the model's dtype).  The
+ * pair is computed as for qdm_quantize_affine, each value rounded once to bf16
+ * (nearest-even), then every code chosen against the rounded pair:
+ *   q = clamp(nearbyint(((double)w - bias_bf16) / scale_bf16), 0, 2^bits - 1)
+ * (all 0 when the rounded scale is 0).  bits 4 or 8 (storage as for the fp32
+ * pairs); scale_bias_out host uint16 [n][k/group][2].  Bit-exact. */
+int qdm_quantize_pack_rows_sb16(const float* w, int32_t n, int32_t k, int32_t bits, int32_t group, void* q_out,
+                                uint16_t* scale_bias_out);
+
+/* The same for a gate/up pair: interleaved codes and bf16 pairs [ffn][2][d/group][2]. */
+int qdm_quantize_pack_gate_up_sb16(const float* w_gate, const float* w_up, int32_t ffn, int32_t d, int32_t bits,
+                                   int32_t group, void* q_out, uint16_t* scale_bias_out);
 
 /* MX quantizer (the pages name the formats, not a quantizer; this is the OCP
  * Microscaling conversion, the plain reading): per block of 32,

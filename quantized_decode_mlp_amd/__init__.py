@@ -27,6 +27,7 @@ QDM_ERR_HIP = -5
 
 QDM_F32, QDM_F16, QDM_BF16 = 0, 1, 2
 QDM_MXFP4, QDM_MXFP8 = 0x104, 0x108       # qdm_weight.bits of the MX block-scaled formats
+QDM_U4_SB16, QDM_U8_SB16 = 0x204, 0x208   # affine 4/8-bit with bf16 (scale, bias) pairs
 
 # Every symbol include/qdm.h declares (checked by the tests).
 EXPORTS = (
@@ -36,6 +37,7 @@ EXPORTS = (
     "qdm_gemv_gate_up_swiglu", "qdm_gemv_down_residual", "qdm_gemv_linear", "qdm_mlp_decode",
     "qdm_add_rmsnorm", "qdm_mlp_rmsnorm_workspace_bytes", "qdm_mlp_decode_rmsnorm",
     "qdm_mx_scale_bytes", "qdm_quantize_mx", "qdm_quantize_mx_gate_up",
+    "qdm_quantize_pack_rows_sb16", "qdm_quantize_pack_gate_up_sb16",
     "qdm_status_string", "qdm_version",
 )
 
@@ -82,6 +84,8 @@ def _load():
         "qdm_mlp_decode_rmsnorm": (ctypes.c_int, [vp, vp, vp, f32, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
                                                   ctypes.POINTER(qdm_weight), vp, sz, vp, vp, vp]),
         "qdm_mx_scale_bytes": (sz, [i32, i32]),
+        "qdm_quantize_pack_rows_sb16": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp]),
+        "qdm_quantize_pack_gate_up_sb16": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, vp, vp]),
         "qdm_quantize_mx": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         "qdm_quantize_mx_gate_up": (ctypes.c_int, [vp, vp, i32, i32, i32, vp, vp]),
         "qdm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -192,6 +196,30 @@ def quantize_pack_gate_up(w_gate, w_up, bits: int, group: int):
     q, sb = _out_buffers(ffn, d, bits, group, rows_mult=2)
     _check(_lib.qdm_quantize_pack_gate_up(_ptr(wg), _ptr(wu), ffn, d, bits, group, _ptr(q), _ptr(sb)),
            "qdm_quantize_pack_gate_up")
+    return q.reshape(ffn, 2, -1), sb.reshape(ffn, 2, d // group, 2)
+
+
+def quantize_pack_rows_sb16(w, bits: int, group: int):
+    """fp32 [n, k] -> (codes uint8 [n, k*bits/8], bf16 (scale, bias) uint16 [n, k/g, 2])."""
+    w = _host(w, np.float32)
+    n, k = w.shape
+    q = np.empty(packed_q_bytes(n, k, bits), np.uint8)
+    sb = np.empty(scale_bias_floats(n, k, group), np.uint16)
+    _check(_lib.qdm_quantize_pack_rows_sb16(_ptr(w), n, k, bits, group, _ptr(q), _ptr(sb)),
+           "qdm_quantize_pack_rows_sb16")
+    return q.reshape(n, -1), sb.reshape(n, k // group, 2)
+
+
+def quantize_pack_gate_up_sb16(w_gate, w_up, bits: int, group: int):
+    """-> (codes uint8 [ffn, 2, d*bits/8], bf16 pairs uint16 [ffn, 2, d/g, 2])."""
+    wg, wu = _host(w_gate, np.float32), _host(w_up, np.float32)
+    if wg.shape != wu.shape:
+        raise ValueError("gate and up shapes differ")
+    ffn, d = wg.shape
+    q = np.empty(2 * packed_q_bytes(ffn, d, bits), np.uint8)
+    sb = np.empty(2 * scale_bias_floats(ffn, d, group), np.uint16)
+    _check(_lib.qdm_quantize_pack_gate_up_sb16(_ptr(wg), _ptr(wu), ffn, d, bits, group, _ptr(q), _ptr(sb)),
+           "qdm_quantize_pack_gate_up_sb16")
     return q.reshape(ffn, 2, -1), sb.reshape(ffn, 2, d // group, 2)
 
 
@@ -307,8 +335,12 @@ class Weight:
                   block_scales: Optional[np.ndarray] = None):
         torch = _torch()
         qt = torch.from_numpy(np.ascontiguousarray(q).view(np.uint8).reshape(-1)).to(device)
-        sbt = None if scale_bias is None else \
-            torch.from_numpy(np.ascontiguousarray(scale_bias, dtype=np.float32).reshape(-1)).to(device)
+        if scale_bias is None:
+            sbt = None
+        elif np.asarray(scale_bias).dtype == np.uint16:   # bf16 pairs: the bytes as they are
+            sbt = torch.from_numpy(np.ascontiguousarray(scale_bias).view(np.uint8).reshape(-1)).to(device)
+        else:
+            sbt = torch.from_numpy(np.ascontiguousarray(scale_bias, dtype=np.float32).reshape(-1)).to(device)
         bst = None if block_scales is None else \
             torch.from_numpy(np.ascontiguousarray(block_scales, dtype=np.uint8).reshape(-1)).to(device)
         return Weight(n, k, bits, group, qt, sbt, bst)
@@ -417,4 +449,5 @@ __all__ = [
     "quantize_affine", "pack_rows", "quantize_pack_rows", "quantize_pack_gate_up", "pack_gate_up",
     "pack_dense_gate_up", "gemv_gate_up_swiglu", "gemv_down_residual", "gemv_linear", "mlp_decode", "add_rmsnorm",
     "mlp_rmsnorm_workspace_bytes", "mlp_decode_rmsnorm", "mx_scale_bytes", "quantize_mx", "quantize_mx_gate_up",
+    "quantize_pack_rows_sb16", "quantize_pack_gate_up_sb16",
 ]

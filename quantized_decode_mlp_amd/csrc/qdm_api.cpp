@@ -27,7 +27,7 @@ int check_weight(const qdm_weight* w) {
         if (w->group != 32) return QDM_ERR_UNSUPPORTED;
         if (w->k % 32) return QDM_ERR_INVALID_ARG;
         if (!w->block_scales) return QDM_ERR_INVALID_ARG;
-    } else if (w->bits == 8 || w->bits == 4) {
+    } else if (w->bits == 8 || w->bits == 4 || w->bits == QDM_U8_SB16 || w->bits == QDM_U4_SB16) {
         if (!(w->group == 32 || w->group == 64 || w->group == 128)) return QDM_ERR_UNSUPPORTED;
         if (w->k % w->group) return QDM_ERR_INVALID_ARG;
         if (!w->scale_bias) return QDM_ERR_INVALID_ARG;
@@ -45,6 +45,10 @@ int hip_status(int e) { return e == 0 ? QDM_OK : QDM_ERR_HIP; }
 
 bool is_mx(int32_t bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
 
+// formats that only the weight-streaming kernels (one row) and the few-row
+// matrix-core streaming kernels take: MX and the bf16-pair affine formats
+bool stream_only(int32_t bits) { return is_mx(bits) || bits == QDM_U4_SB16 || bits == QDM_U8_SB16; }
+
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 size_t act_bytes(int dt) { return dt == QDM_F32 ? 4 : 2; }
@@ -61,7 +65,7 @@ int check_mx_pass(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
 
 // (rows run in passes of at most kPassRows: the full passes and the remainder are checked)
 int check_mx_rows(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
-    if (!is_mx(w->bits)) return QDM_OK;
+    if (!stream_only(w->bits)) return QDM_OK;
     if (m > kPassRows)
         if (int e = check_mx_pass(w, kPassRows, xb, act, kind)) return e;
     const int32_t rem = m % kPassRows;

@@ -28,6 +28,8 @@ int run_chain(const ChainArgs& ch, const qdm_weight& gu, const qdm_weight& dn, f
     switch (gu.bits) {
         case 8: e = run_stream<8, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;
         case 4: e = run_stream<4, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;
+        case QDM_U8_SB16: e = run_stream<QDM_U8_SB16, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;
+        case QDM_U4_SB16: e = run_stream<QDM_U4_SB16, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;
         case QDM_MXFP8: e = run_stream<QDM_MXFP8, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;
         case QDM_MXFP4: e = run_stream<QDM_MXFP4, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;
         default: e = run_stream<16, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;
@@ -36,6 +38,8 @@ int run_chain(const ChainArgs& ch, const qdm_weight& gu, const qdm_weight& dn, f
     switch (dn.bits) {
         case 8: return run_stream<8, DT_F32, XDT, false, kEpiChain>(dn, h, nullptr, out, d, ffn, sd, s, ch);
         case 4: return run_stream<4, DT_F32, XDT, false, kEpiChain>(dn, h, nullptr, out, d, ffn, sd, s, ch);
+        case QDM_U8_SB16: return run_stream<QDM_U8_SB16, DT_F32, XDT, false, kEpiChain>(dn, h, nullptr, out, d, ffn, sd, s, ch);
+        case QDM_U4_SB16: return run_stream<QDM_U4_SB16, DT_F32, XDT, false, kEpiChain>(dn, h, nullptr, out, d, ffn, sd, s, ch);
         case QDM_MXFP8: return run_stream<QDM_MXFP8, DT_F32, XDT, false, kEpiChain>(dn, h, nullptr, out, d, ffn, sd, s, ch);
         case QDM_MXFP4: return run_stream<QDM_MXFP4, DT_F32, XDT, false, kEpiChain>(dn, h, nullptr, out, d, ffn, sd, s, ch);
         default: return run_stream<16, DT_F32, XDT, false, kEpiChain>(dn, h, nullptr, out, d, ffn, sd, s, ch);

@@ -220,6 +220,10 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
             switch (w.bits) {
                 case 8: return run_stream<8, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
                 case 4: return run_stream<4, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
+                case QDM_U8_SB16:
+                    return run_stream<QDM_U8_SB16, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
+                case QDM_U4_SB16:
+                    return run_stream<QDM_U4_SB16, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
                 case QDM_MXFP8:
                     return run_stream<QDM_MXFP8, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
                 case QDM_MXFP4:
@@ -227,7 +231,7 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
                 default: return run_stream<16, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
             }
         }
-        if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);   // MX: streaming kernel only
+        if (is_mx(w.bits) || is_sb16(w.bits)) return static_cast<int>(hipErrorInvalidValue);   // streaming kernel only
         return run_bits<XDT, ODT, 1, GU>(w, x, r, out, n_out, k, 1, s, n_out);
     }
     // 2..16 rows on the matrix cores.  Gate/up with 8/4-bit or MX weights and
@@ -243,7 +247,7 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
         if (mma_stream_down_supported(w, m, ODT))
             return launch_down_mma_stream(static_cast<const float*>(x), r, m, ODT, w, out, s);
     }
-    if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);
+    if (is_mx(w.bits) || is_sb16(w.bits)) return static_cast<int>(hipErrorInvalidValue);
     if (mma_rows_supported(w, m)) {
         if constexpr (GU) {
             if (XDT == DT_BF16) return launch_gate_up_mma(x, m, w, static_cast<float*>(out), s);
@@ -274,6 +278,10 @@ int run_linear(const qdm_weight& w, const void* x, int m, const void* bias, void
         switch (w.bits) {
             case 8: return run_stream<8, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
             case 4: return run_stream<4, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
+            case QDM_U8_SB16:
+                return run_stream<QDM_U8_SB16, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
+            case QDM_U4_SB16:
+                return run_stream<QDM_U4_SB16, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
             case QDM_MXFP8:
                 return run_stream<QDM_MXFP8, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
             case QDM_MXFP4:
@@ -281,7 +289,7 @@ int run_linear(const qdm_weight& w, const void* x, int m, const void* bias, void
             default: return run_stream<16, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
         }
     }
-    if (is_mx(w.bits)) return static_cast<int>(hipErrorInvalidValue);
+    if (is_mx(w.bits) || is_sb16(w.bits)) return static_cast<int>(hipErrorInvalidValue);
     const size_t xe = XDT == DT_F32 ? 4 : 2;
     for (int m0 = 0; m0 < m; m0 += 4) {
         const int mr = m - m0 < 4 ? m - m0 : 4;

@@ -160,7 +160,16 @@ struct StepCodes<QDM_MXFP4, XDT> : StepWords<4> {
     }
 };
 
+// The affine formats with bf16 (scale, bias) pairs take the plain affine codes.
+template <int XDT>
+struct StepCodes<QDM_U8_SB16, XDT> : StepCodes<8, XDT> {};
+template <int XDT>
+struct StepCodes<QDM_U4_SB16, XDT> : StepCodes<4, XDT> {};
+
 constexpr bool mx_bits(int bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
+constexpr bool sb16_bits(int bits) { return bits == QDM_U4_SB16 || bits == QDM_U8_SB16; }
+// affine 4-bit codes (either pair storage): element pairs (e, e + 4), so the staged rows are permuted
+constexpr bool nibble_pairs(int bits) { return bits == 4 || bits == QDM_U4_SB16; }
 constexpr int code_width(int bits) { return bits & 0xff; }
 
 // An E8M0 code as its fp32 power of two (code 0: the subnormal 2^-127).

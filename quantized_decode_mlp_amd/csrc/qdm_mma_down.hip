@@ -101,6 +101,13 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
                     const uint8_t* e = reinterpret_cast<const uint8_t*>(sb) + row * ngroups + gbase + g;
                     const uint32_t e0 = e[0], e1 = e[1];
                     pw[r] = f32x4{e8m0_value(e0), 0.f, e8m0_value(e1), 0.f};
+                } else if constexpr (sb16_bits(BITS)) {
+                    // bf16 pairs: the two groups' (scale, bias) in 8 bytes
+                    const u32x2 p2 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(sb) +
+                                                                    (row * ngroups + gbase + g) * 4);
+                    const uint32_t p0 = p2[0], p1 = p2[1];
+                    pw[r] = f32x4{bf16_to_f32(p0 & 0xffffu), bf16_to_f32(p0 >> 16), bf16_to_f32(p1 & 0xffffu),
+                                  bf16_to_f32(p1 >> 16)};
                 } else {
                     pw[r] = *reinterpret_cast<const f32x4*>(sb + 2 * (row * ngroups + gbase + g));
                 }
@@ -165,7 +172,7 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // element pairs (2i, 2i+1), or (i, i+4) for 4-bit codes
-                const int ea = BITS == 4 ? i : 2 * i, eb = BITS == 4 ? i + 4 : 2 * i + 1;
+                const int ea = nibble_pairs(BITS) ? i : 2 * i, eb = nibble_pairs(BITS) ? i + 4 : 2 * i + 1;
                 oh[i] = pack2(hi[ea], hi[eb]);
                 ol[i] = pack2(lo[ea], lo[eb]);
             }
@@ -388,6 +395,8 @@ template <int ODT>
 int run_down_b(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* rc) {
     switch (w.bits) {
         case 8: return run_down_g<8, ODT>(w, h, r, out, m, s, rc);
+        case QDM_U8_SB16: return run_down_g<QDM_U8_SB16, ODT>(w, h, r, out, m, s, rc);
+        case QDM_U4_SB16: return run_down_g<QDM_U4_SB16, ODT>(w, h, r, out, m, s, rc);
         case QDM_MXFP8: return run_down<QDM_MXFP8, 32, ODT>(w, h, r, out, m, s, rc);
         case QDM_MXFP4: return run_down<QDM_MXFP4, 32, ODT>(w, h, r, out, m, s, rc);
         default: return run_down_g<4, ODT>(w, h, r, out, m, s, rc);
@@ -404,13 +413,13 @@ bool split_exists(int m, int n, int k) {
 
 bool mma_stream_down_supported(const qdm_weight& w, int m, int act) {
     if (m < 2 || m > kRows) return false;
-    if (w.bits != 8 && w.bits != 4 && !mx_bits(w.bits)) return false;
+    if (w.bits != 8 && w.bits != 4 && !mx_bits(w.bits) && !sb16_bits(w.bits)) return false;
     if (w.group != 32 && w.group != 64 && w.group != 128) return false;
     if (act != DT_BF16 && act != DT_F16) return false;   // h enters at ~16 bits: 16-bit outputs only
     if (w.n % kRows != 0) return false;
     if (w.bits == QDM_MXFP8) return w.group == 32 && split_exists<QDM_MXFP8, 32>(m, w.n, w.k);
     if (w.bits == QDM_MXFP4) return w.group == 32 && split_exists<QDM_MXFP4, 32>(m, w.n, w.k);
-    if (w.bits == 4)
+    if (code_width(w.bits) == 4)
         return w.group == 32 ? split_exists<4, 32>(m, w.n, w.k)
              : w.group == 64 ? split_exists<4, 64>(m, w.n, w.k) : split_exists<4, 128>(m, w.n, w.k);
     return w.group == 32 ? split_exists<8, 32>(m, w.n, w.k)

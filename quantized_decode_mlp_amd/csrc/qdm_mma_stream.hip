@@ -137,6 +137,13 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
                         const uint8_t* e = reinterpret_cast<const uint8_t*>(sb) + row * ngroups + gbase + g;
                         const uint32_t e0 = e[0], e1 = e[1];
                         pw[v][r] = f32x4{e8m0_value(e0), 0.f, e8m0_value(e1), 0.f};
+                    } else if constexpr (sb16_bits(BITS)) {
+                        // bf16 pairs: the two groups' (scale, bias) in 8 bytes
+                        const u32x2 p2 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(sb) +
+                                                                        (row * ngroups + gbase + g) * 4);
+                        const uint32_t p0 = p2[0], p1 = p2[1];
+                        pw[v][r] = f32x4{bf16_to_f32(p0 & 0xffffu), bf16_to_f32(p0 >> 16), bf16_to_f32(p1 & 0xffffu),
+                                         bf16_to_f32(p1 >> 16)};
                     } else {
                         pw[v][r] = *reinterpret_cast<const f32x4*>(sb + 2 * (row * ngroups + gbase + g));
                     }
@@ -192,7 +199,7 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
             m = u / ppr;
             c = u - m * ppr;
             u32x4 o = v;
-            if constexpr (BITS == 4) {
+            if constexpr (nibble_pairs(BITS)) {
                 // elements (0, 4), (1, 5), (2, 6), (3, 7) of the piece per word
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -433,6 +440,8 @@ template <int XDT, bool NORM>
 int run_gate_up_x(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s, const NormArgs& na) {
     switch (w.bits) {
         case 8: return run_gate_up_g<8, XDT, NORM>(w, x, h, m, s, na);
+        case QDM_U8_SB16: return run_gate_up_g<QDM_U8_SB16, XDT, NORM>(w, x, h, m, s, na);
+        case QDM_U4_SB16: return run_gate_up_g<QDM_U4_SB16, XDT, NORM>(w, x, h, m, s, na);
         case QDM_MXFP8: return run_gate_up<QDM_MXFP8, XDT, 32, NORM>(w, x, h, m, s, na);
         case QDM_MXFP4: return run_gate_up<QDM_MXFP4, XDT, 32, NORM>(w, x, h, m, s, na);
         default: return run_gate_up_g<4, XDT, NORM>(w, x, h, m, s, na);
@@ -443,11 +452,12 @@ int run_gate_up_x(const qdm_weight& w, const void* x, float* h, int m, hipStream
 
 bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
     if (m < 2 || m > kRows) return false;
-    if (w.bits != 8 && w.bits != 4 && !mx_bits(w.bits)) return false;
+    if (w.bits != 8 && w.bits != 4 && !mx_bits(w.bits) && !sb16_bits(w.bits)) return false;
     if (w.group != 32 && w.group != 64 && w.group != 128) return false;
     if (mx_bits(w.bits) && w.group != 32) return false;
     if (act != DT_BF16 && act != DT_F16) return false;
-    const int kbk = (w.bits == 4 && w.group >= 64) ? 128 : 64;
+    const int cw = code_width(w.bits);
+    const int kbk = (cw == 4 && w.group >= 64) ? 128 : 64;
     if (w.n % kRows != 0 || w.k % (kbk * kS) != 0) return false;
     // each wave's groups: a whole, even number, at most 8 per pair register
     const int gw = w.k / kS / w.group;
@@ -455,7 +465,7 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
     if (gw * w.group * kS != w.k || gw % 2 != 0 || gw > 8 * npl) return false;
     // staged rows, chunk sums and the combine buffer within one CU's LDS
     const size_t dyn = mx_bits(w.bits) ? gate_up_lds_bytes<QDM_MXFP8, 32>(m, w.k)
-                     : w.bits == 4 ? (w.group == 32 ? gate_up_lds_bytes<4, 32>(m, w.k)
+                     : cw == 4 ? (w.group == 32 ? gate_up_lds_bytes<4, 32>(m, w.k)
                                       : w.group == 64 ? gate_up_lds_bytes<4, 64>(m, w.k)
                                                       : gate_up_lds_bytes<4, 128>(m, w.k))
                                    : (w.group == 32 ? gate_up_lds_bytes<8, 32>(m, w.k)

@@ -106,6 +106,48 @@ bool codes_in_range(const uint8_t* codes, int64_t count, int32_t bits) {
     return true;
 }
 
+// bf16 nearest-even of a finite fp32 value, as its 16 bits.
+inline uint16_t bf16_bits(float f) {
+    uint32_t u = 0;
+    std::memcpy(&u, &f, 4);
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+inline double bf16_value(uint16_t b) {
+    const uint32_t u = static_cast<uint32_t>(b) << 16;
+    float f = 0.0f;
+    std::memcpy(&f, &u, 4);
+    return static_cast<double>(f);
+}
+
+// Quantizes and packs one row with bf16 (scale, bias) pairs: the group's fp32
+// pair as in quantize_group, each rounded once to bf16, then the codes chosen
+// against the rounded pair.
+void quantize_pack_row_sb16(const float* w, int32_t k, int32_t bits, int32_t group, uint8_t* q_row,
+                            uint16_t* sb_row, uint8_t* scratch) {
+    const int32_t qmax = (1 << bits) - 1;
+    for (int32_t j = 0; j < k / group; ++j) {
+        const float* g = w + static_cast<int64_t>(j) * group;
+        uint8_t* c = scratch + static_cast<int64_t>(j) * group;
+        float sc = 0.0f, bi = 0.0f;
+        quantize_group(g, group, qmax, c, &sc, &bi);
+        const uint16_t sb = bf16_bits(sc), bb = bf16_bits(bi);
+        sb_row[2 * j] = sb;
+        sb_row[2 * j + 1] = bb;
+        const double s = bf16_value(sb), b = bf16_value(bb);
+        for (int32_t i = 0; i < group; ++i) {
+            if (s == 0.0) {
+                c[i] = 0;
+                continue;
+            }
+            double q = std::nearbyint((static_cast<double>(g[i]) - b) / s);
+            q = q < 0.0 ? 0.0 : (q > qmax ? static_cast<double>(qmax) : q);
+            c[i] = static_cast<uint8_t>(q);
+        }
+    }
+    pack_row_codes(scratch, k, bits, q_row);
+}
+
 // MX block-scaled formats: blocks of 32 along k, an E8M0 scale per block,
 // E2M1 (MXFP4) or E4M3 (MXFP8) elements -- the OCP Microscaling formats the
 // pages' MXFP4 / MXFP8 name ("MLX-LM Backend", "Block-Scaled MLX Primitive").
@@ -172,6 +214,46 @@ void quantize_mx_row(const float* w, int32_t k, int32_t bits, uint8_t* q_row, ui
 
 extern "C" {
 
+int qdm_quantize_pack_rows_sb16(const float* w, int32_t n, int32_t k, int32_t bits, int32_t group, void* q_out,
+                                uint16_t* scale_bias_out) {
+    if (!w || !q_out || !scale_bias_out || n <= 0 || k <= 0 || group <= 0) return QDM_ERR_INVALID_ARG;
+    if (!valid_bits_group(bits, group)) return QDM_ERR_UNSUPPORTED;
+    if (k % group) return QDM_ERR_INVALID_ARG;
+    if (!all_finite(w, static_cast<int64_t>(n) * k)) return QDM_ERR_INVALID_ARG;
+    const int32_t ng = k / group;
+    const int64_t rb = static_cast<int64_t>(k) * bits / 8;
+    auto* q = static_cast<uint8_t*>(q_out);
+    parallel_rows(n, k, [&](int64_t b, int64_t e) {
+        std::vector<uint8_t> scratch(static_cast<size_t>(k));
+        for (int64_t i = b; i < e; ++i)
+            quantize_pack_row_sb16(w + i * k, k, bits, group, q + i * rb, scale_bias_out + 2 * i * ng, scratch.data());
+    });
+    return QDM_OK;
+}
+
+int qdm_quantize_pack_gate_up_sb16(const float* w_gate, const float* w_up, int32_t ffn, int32_t d, int32_t bits,
+                                   int32_t group, void* q_out, uint16_t* scale_bias_out) {
+    if (!w_gate || !w_up || !q_out || !scale_bias_out || ffn <= 0 || d <= 0 || group <= 0)
+        return QDM_ERR_INVALID_ARG;
+    if (!valid_bits_group(bits, group)) return QDM_ERR_UNSUPPORTED;
+    if (d % group) return QDM_ERR_INVALID_ARG;
+    const int64_t nd = static_cast<int64_t>(ffn) * d;
+    if (!all_finite(w_gate, nd) || !all_finite(w_up, nd)) return QDM_ERR_INVALID_ARG;
+    const int32_t ng = d / group;
+    const int64_t rb = static_cast<int64_t>(d) * bits / 8;
+    auto* q = static_cast<uint8_t*>(q_out);
+    parallel_rows(ffn, 2 * static_cast<int64_t>(d), [&](int64_t b, int64_t e) {
+        std::vector<uint8_t> scratch(static_cast<size_t>(d));
+        for (int64_t f = b; f < e; ++f) {
+            quantize_pack_row_sb16(w_gate + f * d, d, bits, group, q + (2 * f) * rb, scale_bias_out + (2 * f) * 2 * ng,
+                                   scratch.data());
+            quantize_pack_row_sb16(w_up + f * d, d, bits, group, q + (2 * f + 1) * rb,
+                                   scale_bias_out + (2 * f + 1) * 2 * ng, scratch.data());
+        }
+    });
+    return QDM_OK;
+}
+
 size_t qdm_mx_scale_bytes(int32_t n, int32_t k) {
     if (n <= 0 || k <= 0 || k % kMxBlock) return 0;
     return static_cast<size_t>(n) * static_cast<size_t>(k / kMxBlock);
@@ -219,6 +301,8 @@ size_t qdm_packed_q_bytes(int32_t n, int32_t k, int32_t bits) {
     if (bits == 8) return nk;
     if (bits == 4) return (k % 2) ? 0 : nk / 2;
     if (bits == 16) return nk * 2;
+    if (bits == QDM_U8_SB16) return nk;
+    if (bits == QDM_U4_SB16) return (k % 2) ? 0 : nk / 2;
     if (bits == QDM_MXFP8) return nk;
     if (bits == QDM_MXFP4) return (k % 2) ? 0 : nk / 2;
     return 0;

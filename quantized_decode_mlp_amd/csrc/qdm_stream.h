@@ -79,9 +79,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
 
-// BITS is the weight format: 4 / 8 (affine), 16 (dense bf16), QDM_MXFP4 /
-// QDM_MXFP8 (block-scaled; their low byte is the code width).
+// BITS is the weight format: 4 / 8 (affine), 16 (dense bf16), QDM_U4_SB16 /
+// QDM_U8_SB16 (affine, bf16 pairs), QDM_MXFP4 / QDM_MXFP8 (block-scaled);
+// the low byte is the code width.
 constexpr bool is_mx(int bits) { return bits == QDM_MXFP4 || bits == QDM_MXFP8; }
+constexpr bool is_sb16(int bits) { return bits == QDM_U4_SB16 || bits == QDM_U8_SB16; }
 constexpr int code_bits(int bits) { return bits & 0xff; }
 
 template <int BITS>
@@ -109,7 +111,8 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     constexpr int NV = GU ? 2 : 1;
     constexpr bool MX = is_mx(BITS);
     constexpr int CB = code_bits(BITS);
-    constexpr bool AFFINE = BITS == 4 || BITS == 8;
+    constexpr bool SB16 = is_sb16(BITS);                 // affine with bf16 (scale, bias) pairs
+    constexpr bool AFFINE = (CB == 4 || CB == 8) && !MX;
     constexpr int NT = 64 * S * P;
     constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
     constexpr bool NORM = EPI == kEpiChain && GU;   // the activation row is rmsnorm(a + b) * w
@@ -164,11 +167,12 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         vj[j] = c < C;
         const uint32_t cc = static_cast<uint32_t>(vj[j] ? c : C - 1);
         qoff[j] = cc * 16u;
-        soff[j] = AFFINE ? ((cc * E) >> gshift) * 8u : MX ? (cc * E) >> 5 : 0u;
+        soff[j] = AFFINE ? ((cc * E) >> gshift) * (SB16 ? 4u : 8u) : MX ? (cc * E) >> 5 : 0u;
     }
 
-    // per chunk: the affine (scale, bias) pair, or the MX block's E8M0 code
-    using ChunkScale = typename std::conditional<MX, uint32_t, f32x2>::type;
+    // per chunk: the affine (scale, bias) pair (fp32, or two bf16 in a dword),
+    // or the MX block's E8M0 code; decoded where used, so no load is waited on early
+    using ChunkScale = typename std::conditional<MX || SB16, uint32_t, f32x2>::type;
     u32x4 wbuf[NV][TW];
     ChunkScale pbuf[NV][TW];
 
@@ -179,11 +183,14 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         for (int v = 0; v < NV; ++v) {
             const uint32_t prow = GU ? 2u * row + v : row;
             const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
-            const uint8_t* srow = reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * (MX ? nbk : ng * 8);
+            const uint8_t* srow =
+                reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * (MX ? nbk : ng * (SB16 ? 4 : 8));
 #pragma unroll
             for (int j = 0; j < TW; ++j) {
                 wq[v][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + qoff[j]));
-                if constexpr (AFFINE)
+                if constexpr (SB16)
+                    pp[v][j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(srow + soff[j]));
+                else if constexpr (AFFINE)
                     pp[v][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(srow + soff[j]));
                 else if constexpr (MX)
                     pp[v][j] = __builtin_nontemporal_load(srow + soff[j]);
@@ -300,7 +307,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 #pragma unroll
             for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(xv[j][e]));
         const int sg = 15 - __builtin_amdgcn_frexp_expf(m);
-        nsg = BITS == 8 ? -sg : 4 - sg;
+        nsg = CB == 8 ? -sg : 4 - sg;
 #pragma unroll
         for (int j = 0; j < TW; ++j) {
             _Float16 hv[E];
@@ -312,8 +319,8 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int h = 0; h < E / 8; ++h) {
-                    const int a = BITS == 8 ? 4 * i + 2 * h : 8 * i + h;
-                    const int b = BITS == 8 ? a + 1 : a + 4;
+                    const int a = CB == 8 ? 4 * i + 2 * h : 8 * i + h;
+                    const int b = CB == 8 ? a + 1 : a + 4;
                     xp[j][i * (E / 8) + h] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[a])) |
                                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hv[b])) << 16);
                 }
@@ -325,7 +332,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
             for (int i = 0; i < E / 2; ++i)
                 t = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, xp[j][i]), __builtin_bit_cast(h16x2, 0x3c003c00u), t,
                                            false);
-            xoff[j] = (BITS == 8 ? 1024.f : 1.f) * t;
+            xoff[j] = (CB == 8 ? 1024.f : 1.f) * t;
             xs[j] = __builtin_amdgcn_ldexpf(t, -sg);
         }
     } else if constexpr (DM == 3) {
@@ -411,7 +418,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t word = wq[v][j][i];
-                    if constexpr (DM == 1 && BITS == 8) {
+                    if constexpr (DM == 1 && CB == 8) {
                         const uint32_t c01 = __builtin_amdgcn_perm(0x64646464u, word, 0x04010400u);
                         const uint32_t c23 = __builtin_amdgcn_perm(0x64646464u, word, 0x04030402u);
                         dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, c01), __builtin_bit_cast(h16x2, xp[j][2 * i]),
@@ -474,8 +481,8 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 #pragma unroll
                         for (int e = 0; e < EPD; ++e) {
                             float c;
-                            if constexpr (BITS == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
-                            else if constexpr (BITS == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
+                            if constexpr (CB == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
+                            else if constexpr (CB == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
                             else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
                             dot = fmaf(c, xv[j][i * EPD + e], dot);
                         }
@@ -486,7 +493,15 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                     const uint32_t e8 = pp[v][j];
                     acc = fmaf(__uint_as_float(e8 ? e8 << 23 : 0x00400000u), dot, acc);
                 } else if constexpr (AFFINE) {
-                    const float sc = pp[v][j].x, bi = pp[v][j].y;
+                    float sc, bi;
+                    if constexpr (SB16) {
+                        const uint32_t pr = pp[v][j];
+                        sc = bf16_to_f32(pr & 0xffffu);
+                        bi = bf16_to_f32(pr >> 16);
+                    } else {
+                        sc = pp[v][j].x;
+                        bi = pp[v][j].y;
+                    }
                     if constexpr (DM == 1) {
                         acc = fmaf(sc, dot - xoff[j], acc);
                         acc2 = fmaf(bi, xs[j], acc2);

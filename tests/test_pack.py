@@ -172,3 +172,40 @@ def test_mx_rejects():
     assert q.mx_scale_bytes(4096, 12288) == 4096 * 384
     assert q.mx_scale_bytes(4, 48) == 0
     assert q.packed_q_bytes(4, 64, q.QDM_MXFP4) == 128 and q.packed_q_bytes(4, 64, q.QDM_MXFP8) == 256
+
+
+# ------------------------------------------------------------------ affine with bf16 (scale, bias)
+
+def _bf16_bits(v):
+    return (np.asarray(v, dtype=np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (8, 128), (4, 64), (8, 32), (4, 128)])
+def test_sb16_bit_exact(bits, group):
+    for wl, rows in ((4, 96), (5, 64)):
+        w = W.weight_f32(W.WORKLOADS[wl], "w_down")[:rows]
+        c, s, b = oracle.quantize_affine_bf16sb(w, bits, group)
+        q1, sb1 = q.quantize_pack_rows_sb16(w, bits, group)
+        assert np.array_equal(q1, oracle.pack_codes(c, bits))
+        assert np.array_equal(sb1[..., 0], _bf16_bits(s)) and np.array_equal(sb1[..., 1], _bf16_bits(b))
+
+
+def test_sb16_gate_up_interleave():
+    wg = W.generic_weights((5, 1), 40, 256, 0.02)
+    wu = W.generic_weights((5, 2), 40, 256, 0.02)
+    q1, sb1 = q.quantize_pack_gate_up_sb16(wg, wu, 4, 64)
+    for v, w in enumerate((wg, wu)):
+        c, s, b = oracle.quantize_affine_bf16sb(w, 4, 64)
+        assert np.array_equal(q1[:, v], oracle.pack_codes(c, 4))
+        assert np.array_equal(sb1[:, v, :, 0], _bf16_bits(s)) and np.array_equal(sb1[:, v, :, 1], _bf16_bits(b))
+
+
+def test_sb16_rejects():
+    L = q._lib
+    w = np.zeros((2, 64), np.float32)
+    qb, sb = np.empty(128, np.uint8), np.empty(16, np.uint16)
+    assert L.qdm_quantize_pack_rows_sb16(q._ptr(w), 2, 64, 6, 32, q._ptr(qb), q._ptr(sb)) == q.QDM_ERR_UNSUPPORTED
+    assert L.qdm_quantize_pack_rows_sb16(q._ptr(w), 2, 64, 8, 48, q._ptr(qb), q._ptr(sb)) == q.QDM_ERR_UNSUPPORTED
+    w[0, 1] = np.inf
+    assert L.qdm_quantize_pack_rows_sb16(q._ptr(w), 2, 64, 8, 32, q._ptr(qb), q._ptr(sb)) == q.QDM_ERR_INVALID_ARG
+    assert q.packed_q_bytes(4, 64, q.QDM_U4_SB16) == 128 and q.packed_q_bytes(4, 64, q.QDM_U8_SB16) == 256
