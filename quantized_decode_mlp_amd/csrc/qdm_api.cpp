@@ -66,14 +66,18 @@ int check_mx_pass(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
 // (rows run in passes of at most kPassRows: the full passes and the remainder are checked)
 int check_mx_rows(const qdm_weight* w, int32_t m, int xb, int act, int kind) {
     if (!stream_only(w->bits)) return QDM_OK;
+    if (kind != 2 && qdm::prefill_supported(*w, m, act)) return QDM_OK;
     if (m > kPassRows)
         if (int e = check_mx_pass(w, kPassRows, xb, act, kind)) return e;
     const int32_t rem = m % kPassRows;
     return check_mx_pass(w, m <= kPassRows ? m : (rem ? rem : kPassRows), xb, act, kind);
 }
 
-// The device calls over row passes of at most kPassRows rows (each pass streams the weights).
+// The device calls: one tiled launch for more than kPassRows rows where the
+// prefill kernels take the weight, otherwise row passes of at most kPassRows
+// rows (each pass streams the weights).
 int gate_up_passes(const void* x, int32_t m, int act, const qdm_weight& gu, float* h, void* stream) {
+    if (qdm::prefill_supported(gu, m, act)) return qdm::launch_gate_up_prefill(x, m, act, gu, h, stream);
     const size_t xe = act_bytes(act);
     for (int32_t m0 = 0; m0 < m; m0 += kPassRows) {
         const int32_t mr = std::min(kPassRows, m - m0);
@@ -85,6 +89,7 @@ int gate_up_passes(const void* x, int32_t m, int act, const qdm_weight& gu, floa
 }
 
 int down_passes(const float* h, const void* r, int32_t m, int act, const qdm_weight& dn, void* out, void* stream) {
+    if (qdm::prefill_supported(dn, m, act)) return qdm::launch_down_prefill(h, r, m, act, dn, out, stream);
     const size_t oe = act_bytes(act);
     for (int32_t m0 = 0; m0 < m; m0 += kPassRows) {
         const int32_t mr = std::min(kPassRows, m - m0);

@@ -2,6 +2,7 @@
 // HIP launchers (qdm_*.hip).  Arguments are already validated when these run.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "qdm.h"
@@ -42,6 +43,14 @@ int launch_down_mma_stream(const float* h, const void* r, int m, int act, const 
 bool chain_stream_supported(const qdm_weight& gu, const qdm_weight& dn, int act);
 int launch_mlp_chain_stream(const void* a, const void* b, const void* w, float eps, int act, const qdm_weight& gu,
                             const qdm_weight& dn, float* h, void* s_out, void* out, void* stream);
+// The device's fp32 partials buffer (at least bytes), shared by the split-K
+// kernels; grows outside graph capture only.  Null with err set on failure.
+float* partials_scratch(size_t bytes, void* stream, int& err);
+// More than 16 rows, 8/4-bit affine (either pair storage) or MX weights, 16-bit
+// activations: tiled dual GEMM, 64 rows x 64 outputs per block (qdm_prefill.hip).
+bool prefill_supported(const qdm_weight& w, int m, int act);
+int launch_gate_up_prefill(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream);
+int launch_down_prefill(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, void* stream);
 int launch_add_rmsnorm(const void* a, const void* b, const void* w, int rows, int n, float eps,
                        int dtype, void* s_out, void* n_out, void* stream);
 

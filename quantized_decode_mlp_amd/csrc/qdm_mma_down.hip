@@ -313,10 +313,13 @@ bool pick_down_split(int m, int n, int k, int cus, DownSplit& out) {
     return found;
 }
 
+}  // namespace
+
 // Partials scratch, one per device, grown on demand.  Growth happens only
 // outside graph capture and after the device has drained, since work on any
 // stream may still use the old buffer.
-float* down_scratch(size_t bytes, hipStream_t s, int& err) {
+float* partials_scratch(size_t bytes, void* stream, int& err) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
     static std::mutex mu;
     static std::map<int, std::pair<void*, size_t>> bufs;
     err = 0;
@@ -352,6 +355,8 @@ float* down_scratch(size_t bytes, hipStream_t s, int& err) {
     return static_cast<float*>(p);
 }
 
+namespace {
+
 template <int BITS, int G, int ODT>
 int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* r_copy) {
     constexpr int NT = 64 * kDS * kDP;
@@ -363,7 +368,7 @@ int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int 
     if (!pick_down_split<BITS, G>(m, w.n, w.k, cus, sp)) return static_cast<int>(hipErrorInvalidValue);
     const int ns = w.k / sp.kr;
     int err = 0;
-    float* part = down_scratch(static_cast<size_t>(ns) * m * w.n * sizeof(float), s, err);
+    float* part = partials_scratch(static_cast<size_t>(ns) * m * w.n * sizeof(float), s, err);
     if (!part) return err;
     auto kern = qmm_down_part_kernel<BITS, G, kDS, kDP, U, pair_regs<G>()>;
     const size_t lds = down_lds_bytes<BITS, G>(m, sp.kr);

@@ -1,0 +1,479 @@
+// Multi-row prefill (more than 16 rows): tiled dual GEMM on the gfx950 matrix
+// cores, the weights read once per 64 activation rows instead of once per 16.
+//
+// Pages: meTile docs, "MLX-LM Backend", section "Dispatch Policy": multi-row
+// calls run a fused dual-GEMM gate/up kernel with register-resident SwiGLU
+// that reuses activation fragments for both GEMMs and stores only the final
+// hidden tile, with row-masked loads and stores for ragged tiles.
+// Quantization: MLX-LM affine groups, w = scale * q + bias; MX block scales.
+//
+// Tile.  A block is four waves over 64 activation rows (four 16-row MMA
+// tiles); wave w owns NO 16-output fragments, outputs n0 + 16 j + 0..15 with
+// n0 = block base + 16 NO w (for gate/up each output has a gate and an up
+// fragment, so a wave holds 2 NO weight fragments).  Every activation
+// fragment read from LDS feeds all of the wave's weight fragments.
+//
+// Chunked k layout.  The K loop runs over k-blocks of KBK k (16 code bytes per
+// lane and weight fragment); a k-block is NF fold chunks of FG = min(G, KBK)
+// k and every 32-k MMA step lies inside one chunk: in chunk c, lane slot kq
+// (lane / 16) holds the FG/4 consecutive k from c FG + kq FG/4, step s of the
+// chunk takes eight of them.  So each code load is one contiguous piece per
+// lane and chunk, and no MMA runs on masked lanes.  The codes enter the MMA as
+// exact operands (StepCodes) and each chunk's partial tile P is folded in fp32
+// as scale * P + (bias - scale * off) * X, X the chunk's activation sum.
+//
+// Pipeline.  The activation k-block is staged in one of two LDS buffers (with
+// the chunk sums) while the other is computed on, one barrier per k-block;
+// activation loads run one k-block ahead in registers, weight loads two.
+//
+// Split K.  When the output tiles alone do not fill the chip, the k-blocks
+// are split over S slices; a slice's tile goes to fp32 partials
+// part[s][m][n'] in the library's device scratch and a second kernel adds the
+// slices in order (so results do not depend on timing) and applies SwiGLU
+// (gate/up) or the residual and the output rounding (down).
+//
+// Gate/up takes the activations in their own 16-bit type; down takes the fp32
+// hidden rows as a bf16 high part and the bf16 remainder (two MMAs per
+// fragment and step, about 16 significant bits).
+#include "qdm_internal.h"
+#include "qdm_launch.h"
+#include "qdm_mma_common.h"
+
+namespace qdm {
+namespace {
+
+constexpr int kPA = 4;            // 16-row activation tiles per block
+constexpr int kPW = 4;            // waves per block
+constexpr int kPBM = 16 * kPA;    // activation rows per block
+constexpr int kPT = 64 * kPW;     // threads per block
+
+template <int BITS, int G>
+struct TileLayout {
+    static constexpr int CB = code_width(BITS);
+    static constexpr int KBK = CB == 4 ? 128 : 64;
+    static constexpr int FG = G < KBK ? G : KBK;   // fold chunk
+    static constexpr int NF = KBK / FG;
+    static constexpr int SPC = FG / 32;            // MMA steps per chunk
+    static constexpr int LB = FG / 4 * CB / 8;     // code bytes per lane and chunk: 4, 8 or 16
+    static_assert(LB == 4 || LB == 8 || LB == 16, "chunk piece size");
+};
+
+// Dynamic LDS: two buffers of NH staged parts [64][KBK + pad] (16-bit), then
+// two buffers of chunk sums [NF][64].
+template <int BITS, int G, bool GU>
+constexpr size_t prefill_lds_bytes() {
+    using L = TileLayout<BITS, G>;
+    return 2 * (GU ? 1 : 2) * static_cast<size_t>(kPBM) * (L::KBK + kPad) * 2 +
+           2 * static_cast<size_t>(L::NF) * kPBM * 4;
+}
+
+template <int BITS, int G, int XDT, bool GU, int ODT, int NO>
+__global__ void __launch_bounds__(kPT)
+qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, const void* __restrict__ xin,
+                   const void* __restrict__ resid, void* __restrict__ out, float* __restrict__ part, int N, int K,
+                   int M, int S) {
+    using L = TileLayout<BITS, G>;
+    constexpr int MDT = GU ? XDT : DT_BF16;   // the MMA's operand type
+    using SC = StepCodes<BITS, MDT>;
+    constexpr int KBK = L::KBK, NF = L::NF, FG = L::FG, SPC = L::SPC, LB = L::LB;
+    constexpr bool MX = mx_bits(BITS), SB16 = sb16_bits(BITS);
+    constexpr int NV = GU ? 2 * NO : NO;      // weight fragments per wave
+    constexpr int NH = GU ? 1 : 2;            // staged parts: the activations, or h's hi and lo
+    constexpr int PPR = KBK / 8;              // 8-element pieces of a staged row
+    constexpr int PT = kPBM * PPR / kPT;      // pieces per thread and k-block
+    constexpr int CPF = FG / 8;               // pieces per fold chunk
+    constexpr int LDA = KBK + kPad;
+    constexpr int XBUF = NH * kPBM * LDA;     // uint16 per staging buffer
+    static_assert(PT * kPT == kPBM * PPR, "pieces split evenly");
+    using PairRaw = typename std::conditional<MX || SB16, uint32_t, f32x2>::type;
+
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+    float* xsum = reinterpret_cast<float*>(lds + 2 * XBUF * 2);
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, kq = lane >> 4;
+    const int slice = static_cast<int>(blockIdx.x) % S;
+    const int nblk = static_cast<int>(blockIdx.x) / S;
+    const int m0 = static_cast<int>(blockIdx.y) * kPBM;
+    const int n0 = (nblk * kPW + w) * 16 * NO;   // this wave's first output
+    const bool wlive = n0 < N;                    // wave-uniform (N % 16 == 0)
+    const int nkb = K / KBK;
+    const int kb0 = static_cast<int>((static_cast<int64_t>(nkb) * slice) / S);
+    const int nk = static_cast<int>((static_cast<int64_t>(nkb) * (slice + 1)) / S) - kb0;   // >= 1
+    const uint32_t rb = static_cast<uint32_t>(K) * L::CB / 8;
+    const int ngroups = K / G;
+
+    // weight rows of the wave's fragments (fragments past N read row N - 1 and store nothing)
+    uint32_t wrow[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int j = GU ? v >> 1 : v;
+        const int n = min(n0 + 16 * j + li, N - 1);
+        wrow[v] = GU ? 2u * static_cast<uint32_t>(n) + (v & 1) : static_cast<uint32_t>(n);
+    }
+
+    // ---- activation pieces: piece u = tid + j * kPT of the 64 x KBK tile, row u / PPR, piece u % PPR
+    u32x4 ax[GU ? PT : 1];
+    f32x4 ah[GU ? 1 : PT][2];
+    auto load_a = [&](int kb) {
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int u = tid + j * kPT, row = u / PPR, c = u - row * PPR;
+            // rows past M read row 0; stage_a zeroes them (a select here would wait for the load)
+            const size_t off = static_cast<size_t>(m0 + row < M ? m0 + row : 0) * K + kb * KBK + c * 8;
+            if constexpr (GU) {
+                ax[j] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xin) + off);
+            } else {
+                const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(xin) + off);
+                ah[j][0] = src[0];
+                ah[j][1] = src[1];
+            }
+        }
+    };
+    // staged in MMA operand order (pairs (e, e + 4) for 4-bit affine codes), with the chunk sums
+    auto stage_a = [&](int buf) {
+        uint16_t* xb = xs + buf * XBUF;
+        float* xsb = xsum + buf * NF * kPBM;
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {
+            const int u = tid + j * kPT, row = u / PPR, c = u - row * PPR;
+            const bool live = m0 + row < M;
+            float sum = 0.f;
+            if constexpr (GU) {
+                const u32x4 v = live ? ax[j] : u32x4{0u, 0u, 0u, 0u};
+                u32x4 o = v;
+                if constexpr (nibble_pairs(BITS)) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[i] = __builtin_amdgcn_perm(v[2 + (i >> 1)], v[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
+                }
+                *reinterpret_cast<u32x4*>(xb + row * LDA + c * 8) = o;
+                if constexpr (!MX) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // the word goes through a scalar: __builtin_bit_cast of a vector
+                        // element expression reinterprets the vector's first element
+                        const uint32_t word = v[i];
+                        if constexpr (XDT == DT_BF16)
+                            sum += __uint_as_float(word << 16) + __uint_as_float(word & 0xffff0000u);
+                        else
+                            sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word),
+                                                         __builtin_bit_cast(h16x2, 0x3c003c00u), sum, false);
+                    }
+                }
+            } else {
+                uint32_t hi[8], lo[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = live ? (e < 4 ? ah[j][0][e] : ah[j][1][e - 4]) : 0.f;
+                    hi[e] = __float_as_uint(v) & 0xffff0000u;   // truncation: the exact top half
+                    lo[e] = __float_as_uint(v - __uint_as_float(hi[e])) & 0xffff0000u;
+                    sum += __uint_as_float(hi[e]) + __uint_as_float(lo[e]);
+                }
+                u32x4 oh, ol;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ea = nibble_pairs(BITS) ? i : 2 * i, eb = nibble_pairs(BITS) ? i + 4 : 2 * i + 1;
+                    oh[i] = (hi[ea] >> 16) | (hi[eb] & 0xffff0000u);
+                    ol[i] = (lo[ea] >> 16) | (lo[eb] & 0xffff0000u);
+                }
+                *reinterpret_cast<u32x4*>(xb + row * LDA + c * 8) = oh;
+                *reinterpret_cast<u32x4*>(xb + (kPBM + row) * LDA + c * 8) = ol;
+            }
+            if constexpr (!MX) {
+#pragma unroll
+                for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
+                if (c % CPF == 0) xsb[(c / CPF) * kPBM + row] = sum;
+            }
+        }
+    };
+
+    // ---- weights: per fragment, the lane's code piece of every chunk and the chunk's pair
+    auto load_b = [&](u32x4 (&cw)[NV], PairRaw (&pr)[NV][NF], int kb) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const uint8_t* qrow = q + static_cast<size_t>(wrow[v]) * rb;
+#pragma unroll
+            for (int c = 0; c < NF; ++c) {
+                const uint8_t* src = qrow + static_cast<uint32_t>(kb * KBK + c * FG + kq * (FG / 4)) * L::CB / 8;
+                if constexpr (LB == 16) {
+                    cw[v] = *reinterpret_cast<const u32x4*>(src);
+                } else if constexpr (LB == 8) {
+                    const u32x2 p = *reinterpret_cast<const u32x2*>(src);
+                    cw[v][2 * c] = p[0];
+                    cw[v][2 * c + 1] = p[1];
+                } else {
+                    cw[v][c] = *reinterpret_cast<const uint32_t*>(src);
+                }
+                const size_t gi = static_cast<size_t>(wrow[v]) * ngroups + (kb * KBK + c * FG) / G;
+                if constexpr (MX)
+                    pr[v][c] = reinterpret_cast<const uint8_t*>(sb)[gi];
+                else if constexpr (SB16)
+                    pr[v][c] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(sb) + gi * 4);
+                else
+                    pr[v][c] = *reinterpret_cast<const f32x2*>(sb + 2 * gi);
+            }
+        }
+    };
+
+    f32x4 acc[kPA][NV];
+#pragma unroll
+    for (int a = 0; a < kPA; ++a)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[a][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf, const u32x4 (&cw)[NV], const PairRaw (&pr)[NV][NF]) {
+        if (!wlive) return;   // wave-uniform
+        const uint16_t* xb = xs + buf * XBUF;
+        const float* xsb = xsum + buf * NF * kPBM;
+#pragma unroll
+        for (int c = 0; c < NF; ++c) {
+            f32x4 pt[kPA][NV];
+#pragma unroll
+            for (int a = 0; a < kPA; ++a)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) pt[a][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < SPC; ++s) {
+                const int t = c * SPC + s;
+                const int ka = c * FG + kq * (FG / 4) + 8 * s;
+                u32x4 bv[NV];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) bv[v] = SC::operand(SC::step(cw[v], t));
+#pragma unroll
+                for (int a = 0; a < kPA; ++a) {
+#pragma unroll
+                    for (int hp = 0; hp < NH; ++hp) {
+                        const u32x4 av = *reinterpret_cast<const u32x4*>(xb + (hp * kPBM + 16 * a + li) * LDA + ka);
+#pragma unroll
+                        for (int v = 0; v < NV; ++v) pt[a][v] = mma<MDT>(av, bv[v], pt[a][v]);
+                    }
+                }
+            }
+            // fold: scale * P + (bias - scale * off) * X
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float se, be;
+                if constexpr (MX) {
+                    se = e8m0_value(pr[v][c]);
+                    be = 0.f;
+                } else if constexpr (SB16) {
+                    const uint32_t p2 = pr[v][c];
+                    se = bf16_to_f32(p2 & 0xffffu) * SC::kInvMul;
+                    be = fmaf(-SC::kOff, se, bf16_to_f32(p2 >> 16));
+                } else {
+                    se = pr[v][c].x * SC::kInvMul;
+                    be = fmaf(-SC::kOff, se, pr[v][c].y);
+                }
+#pragma unroll
+                for (int a = 0; a < kPA; ++a) {
+                    if constexpr (MX) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[a][v][e] = fmaf(se, pt[a][v][e], acc[a][v][e]);
+                    } else {
+                        const f32x4 xc = *reinterpret_cast<const f32x4*>(xsb + c * kPBM + 16 * a + 4 * kq);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[a][v][e] = fmaf(se, pt[a][v][e], fmaf(be, xc[e], acc[a][v][e]));
+                    }
+                }
+            }
+        }
+    };
+
+    // Pipeline, iteration i (compute buffer and weight set i % 2): stage the
+    // activations of k-block i + 1 into the other buffer, issue the weights of
+    // i + 1 into the other set and the activations of i + 2, compute i, barrier.
+    // The next stage waits for the activations, the last loads issued, so every
+    // load has one compute to arrive, and that holds on the first iteration as
+    // on the others (the compiler's wait counts at the loop head take the worse
+    // of the paths into it).  Loads past the slice's end repeat its last
+    // k-block, and idle waves read row N - 1: a load issued on some paths only
+    // would leave the counts unknown and turn every wait into a full drain.  A
+    // block staged past the slice lands in the buffer nobody reads again.  The
+    // loop body is unrolled by two so that every buffer and set index is a
+    // constant.
+    u32x4 cw0[NV], cw1[NV];
+    PairRaw pr0[NV][NF], pr1[NV][NF];
+    load_b(cw0, pr0, kb0);
+    load_a(kb0);
+    stage_a(0);
+    load_a(kb0 + min(1, nk - 1));
+    __syncthreads();
+    auto iter = [&](int i, int buf, const u32x4 (&cw)[NV], const PairRaw (&pr)[NV][NF], u32x4 (&cwn)[NV],
+                    PairRaw (&prn)[NV][NF]) {
+        stage_a(buf ^ 1);
+        load_b(cwn, prn, kb0 + min(i + 1, nk - 1));
+        load_a(kb0 + min(i + 2, nk - 1));
+        if (i < nk) compute(buf, cw, pr);
+        __syncthreads();
+    };
+    for (int i = 0; i < nk; i += 2) {   // uniform per block
+        iter(i, 0, cw0, pr0, cw1, pr1);
+        iter(i + 1, 1, cw1, pr1, cw0, pr0);
+    }
+
+    // epilogue: rows 16a + 4kq + e, output n0 + 16j + li
+    if (!wlive) return;
+    // the residuals first, all loads in flight together (rows and outputs clamped)
+    float rv[GU ? 1 : NO][GU ? 1 : kPA][4];
+    if constexpr (!GU) {
+        if (!part) {
+#pragma unroll
+            for (int j = 0; j < NO; ++j)
+#pragma unroll
+                for (int a = 0; a < kPA; ++a)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = min(m0 + 16 * a + 4 * kq + e, M - 1), n = min(n0 + 16 * j + li, N - 1);
+                        rv[j][a][e] = load_elem<ODT>(resid, static_cast<int64_t>(m) * N + n);
+                    }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+        const int n = n0 + 16 * j + li;
+        if (n >= N) continue;
+#pragma unroll
+        for (int a = 0; a < kPA; ++a) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + 16 * a + 4 * kq + e;
+                if (m >= M) continue;
+                if (part) {
+                    float* prow = part + (static_cast<size_t>(slice) * M + m) * (GU ? 2 * N : N);
+                    if constexpr (GU) {
+                        prow[n] = acc[a][2 * j][e];
+                        prow[N + n] = acc[a][2 * j + 1][e];
+                    } else {
+                        prow[n] = acc[a][j][e];
+                    }
+                } else {
+                    const int64_t o = static_cast<int64_t>(m) * N + n;
+                    if constexpr (GU) {
+                        const float g = acc[a][2 * j][e], u = acc[a][2 * j + 1][e];
+                        static_cast<float*>(out)[o] = g / (1.0f + expf(-g)) * u;
+                    } else {
+                        store_elem<ODT>(out, o, rv[j][a][e] + acc[a][j][e]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The S slices' partials summed in slice order, then SwiGLU (gate/up: part
+// rows hold gate at n and up at N + n) or the residual and the output rounding.
+template <bool GU, int ODT>
+__global__ void __launch_bounds__(256)
+qmm_prefill_reduce_kernel(const float* __restrict__ part, const void* __restrict__ resid, void* __restrict__ out,
+                          int N, int M, int S) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= static_cast<int64_t>(M) * N) return;
+    const int m = static_cast<int>(i / N), n = static_cast<int>(i - static_cast<int64_t>(m) * N);
+    const int64_t W = GU ? 2 * static_cast<int64_t>(N) : N;
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < S; ++s) {
+        const float* p = part + (static_cast<int64_t>(s) * M + m) * W;
+        g += p[n];
+        if constexpr (GU) u += p[N + n];
+    }
+    if constexpr (GU)
+        static_cast<float*>(out)[i] = g / (1.0f + expf(-g)) * u;
+    else
+        store_elem<ODT>(out, i, load_elem<ODT>(resid, i) + g);
+}
+
+constexpr int kNoGateUp = 1;   // output fragments per wave (gate/up)
+constexpr int kNoDown = 2;     // output fragments per wave (down)
+
+// Slices: doubled until there are two blocks per compute unit, each slice
+// keeping at least two k-blocks.
+int pick_slices(int tiles, int nkb, int cus) {
+    int s = 1;
+    while (tiles * s < 2 * cus && 4 * s <= nkb && s < 16) s *= 2;
+    return s;
+}
+
+template <int BITS, int G, int XDT, bool GU, int ODT>
+int run_prefill(const qdm_weight& w, const void* x, const void* r, void* out, int m, hipStream_t s) {
+    constexpr int NO = GU ? kNoGateUp : kNoDown;
+    using L = TileLayout<BITS, G>;
+    auto kern = qmm_prefill_kernel<BITS, G, XDT, GU, ODT, NO>;
+    const float* sbp = mx_bits(BITS) ? reinterpret_cast<const float*>(w.block_scales) : w.scale_bias;
+    if (!sbp) return static_cast<int>(hipErrorInvalidValue);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return static_cast<int>(hipErrorInvalidDevice);
+    const int bn = 16 * NO * kPW;
+    const int nb = (w.n + bn - 1) / bn, mb = (m + kPBM - 1) / kPBM;
+    const int S = pick_slices(nb * mb, w.k / L::KBK, cus);
+    constexpr size_t lds = prefill_lds_bytes<BITS, G, GU>();
+    if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+        return static_cast<int>(hipErrorInvalidValue);
+    float* part = nullptr;
+    if (S > 1) {
+        int err = 0;
+        part = partials_scratch(static_cast<size_t>(S) * m * w.n * (GU ? 2 : 1) * sizeof(float), s, err);
+        if (!part) return err;
+    }
+    hipError_t e = launch(kern, dim3(nb * S, mb), dim3(kPT), lds, s, static_cast<const uint8_t*>(w.q), sbp, x, r,
+                          out, part, w.n, w.k, m, S);
+    if (e != hipSuccess || S == 1) return static_cast<int>(e);
+    const int64_t outs = static_cast<int64_t>(m) * w.n;
+    e = launch(qmm_prefill_reduce_kernel<GU, ODT>, dim3(static_cast<unsigned>((outs + 255) / 256)), dim3(256), 0, s,
+               static_cast<const float*>(part), r, out, w.n, m, S);
+    return static_cast<int>(e);
+}
+
+template <int XDT, bool GU, int ODT, int G>
+int run_prefill_b(const qdm_weight& w, const void* x, const void* r, void* out, int m, hipStream_t s) {
+    switch (w.bits) {
+        case 8: return run_prefill<8, G, XDT, GU, ODT>(w, x, r, out, m, s);
+        case 4: return run_prefill<4, G, XDT, GU, ODT>(w, x, r, out, m, s);
+        case QDM_U8_SB16: return run_prefill<QDM_U8_SB16, G, XDT, GU, ODT>(w, x, r, out, m, s);
+        default: return run_prefill<QDM_U4_SB16, G, XDT, GU, ODT>(w, x, r, out, m, s);
+    }
+}
+
+template <int XDT, bool GU, int ODT>
+int run_prefill_g(const qdm_weight& w, const void* x, const void* r, void* out, int m, hipStream_t s) {
+    if (w.bits == QDM_MXFP8) return run_prefill<QDM_MXFP8, 32, XDT, GU, ODT>(w, x, r, out, m, s);
+    if (w.bits == QDM_MXFP4) return run_prefill<QDM_MXFP4, 32, XDT, GU, ODT>(w, x, r, out, m, s);
+    switch (w.group) {
+        case 32: return run_prefill_b<XDT, GU, ODT, 32>(w, x, r, out, m, s);
+        case 64: return run_prefill_b<XDT, GU, ODT, 64>(w, x, r, out, m, s);
+        default: return run_prefill_b<XDT, GU, ODT, 128>(w, x, r, out, m, s);
+    }
+}
+
+}  // namespace
+
+bool prefill_supported(const qdm_weight& w, int m, int act) {
+    if (m <= kRows) return false;
+    const bool affine = w.bits == 8 || w.bits == 4 || sb16_bits(w.bits);
+    if (!affine && !mx_bits(w.bits)) return false;
+    if (w.group != 32 && w.group != 64 && w.group != 128) return false;
+    if (mx_bits(w.bits) && w.group != 32) return false;
+    if (act != DT_BF16 && act != DT_F16) return false;
+    const int kbk = code_width(w.bits) == 4 ? 128 : 64;
+    return w.n % 16 == 0 && w.k % kbk == 0;
+}
+
+int launch_gate_up_prefill(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return act == DT_F16 ? run_prefill_g<DT_F16, true, DT_F32>(gu, x, nullptr, h, m, s)
+                         : run_prefill_g<DT_BF16, true, DT_F32>(gu, x, nullptr, h, m, s);
+}
+
+int launch_down_prefill(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return act == DT_F16 ? run_prefill_g<DT_F32, false, DT_F16>(dn, h, r, out, m, s)
+                         : run_prefill_g<DT_F32, false, DT_BF16>(dn, h, r, out, m, s);
+}
+
+}  // namespace qdm

@@ -1,5 +1,7 @@
-"""GPU parity with more than 16 rows (the functional multi-row prefill form:
-passes of 16 rows through the few-row kernels) through the C ABI.
+"""GPU parity with more than 16 rows through the C ABI: the tiled prefill
+kernels (64 rows x 64 outputs per block; 8/4-bit affine with either pair
+storage and MX weights, 16-bit activations) and, for the other formats,
+passes of 16 rows through the few-row kernels.
 
 Bars as for the MLP: h within 1e-5 scaled error, y within 5e-3 (bf16) of the
 fp64 oracle; the chain bitwise equal to add + RMSNorm then the MLP."""
@@ -44,12 +46,48 @@ def _check(ow, pw, x, r, act):
     assert ey <= TOL[act], ey
 
 
-@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (16, 0)])
-@pytest.mark.parametrize("m", [17, 40, 64])
-def test_prefill_rows(m, bits, group):
-    print(f"[prefill] m={m} bits={bits} group={group}", flush=True)
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+@pytest.mark.parametrize("bits,group", [(8, 32), (8, 64), (8, 128), (4, 32), (4, 64), (4, 128)])
+@pytest.mark.parametrize("m", [17, 64, 130])
+def test_prefill_rows(m, bits, group, act):
+    """Ragged row tiles (17, 130), one full tile (64); every group width."""
+    print(f"[prefill] m={m} bits={bits} group={group} act={act}", flush=True)
     d, ffn = 1024, 1536
-    ow, pw = generic_case((m, bits, 7), d, ffn, bits, group)
+    ow, pw = generic_case((m, bits, group, 7), d, ffn, bits, group)
+    x = W.generic_act((m, 1), (m, d), act)
+    r = W.generic_act((m, 2), (m, d), act)
+    _check(ow, pw, x, r, act)
+
+
+@pytest.mark.parametrize("m", [17, 40])
+def test_prefill_rows_dense(m):
+    """Dense bf16 weights: passes of 16 rows."""
+    print(f"[prefill] m={m} dense bf16", flush=True)
+    d, ffn = 1024, 1536
+    ow, pw = generic_case((m, 16, 7), d, ffn, 16, 0)
+    x = W.generic_act((m, 1), (m, d), "bf16")
+    r = W.generic_act((m, 2), (m, d), "bf16")
+    _check(ow, pw, x, r, "bf16")
+
+
+def test_prefill_max_rows():
+    """4096 rows, the most a call takes: 64 row tiles."""
+    m, d, ffn = 4096, 256, 512
+    print(f"[prefill] m={m} bits=4 group=64", flush=True)
+    ow, pw = generic_case((m, 4, 7), d, ffn, 4, 64)
+    x = W.generic_act((m, 1), (m, d), "bf16")
+    r = W.generic_act((m, 2), (m, d), "bf16")
+    _check(ow, pw, x, r, "bf16")
+
+
+@pytest.mark.parametrize("d,ffn", [(1024, 1568), (1056, 1536)])
+def test_prefill_outputs_not_a_block_multiple(d, ffn):
+    """Outputs a multiple of 16 but not of 64: the last block has idle waves
+    (gate/up at ffn 1568, down at d 1056; the other projection of each pair
+    has a k the tiled kernel does not take and runs in passes)."""
+    m = 70
+    print(f"[prefill] m={m} d={d} ffn={ffn}", flush=True)
+    ow, pw = generic_case((m, d, ffn), d, ffn, 8, 32)
     x = W.generic_act((m, 1), (m, d), "bf16")
     r = W.generic_act((m, 2), (m, d), "bf16")
     _check(ow, pw, x, r, "bf16")
@@ -109,4 +147,54 @@ def test_prefill_mx_rows():
     y = qdm.mlp_decode(to_device(x), to_device(r), gu, dn)
     torch.cuda.synchronize()
     _, y_ref = oracle.mlp_decode(x.values, r.values, *deq)
+    assert oracle.scaled_error(from_device(y), y_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("bits,group", [(8, 128), (4, 64)])
+def test_prefill_sb16_rows(bits, group):
+    qdm = _qdm()
+    fmt = {8: qdm.QDM_U8_SB16, 4: qdm.QDM_U4_SB16}[bits]
+    m, d, ffn = 90, 1024, 1536
+    print(f"[prefill] m={m} sb16 bits={bits} group={group}", flush=True)
+    g32, u32 = W.generic_weights((m, 21), ffn, d), W.generic_weights((m, 22), ffn, d)
+    d32 = W.generic_weights((m, 23), d, ffn)
+    q, sb = qdm.quantize_pack_gate_up_sb16(g32, u32, bits, group)
+    gu = qdm.Weight.from_host(ffn, d, fmt, group, q, sb)
+    dq, dsb = qdm.quantize_pack_rows_sb16(d32, bits, group)
+    dn = qdm.Weight.from_host(d, ffn, fmt, group, dq, dsb)
+    deq = []
+    for a in (g32, u32, d32):
+        c, s_, b = oracle.quantize_affine_bf16sb(a, bits, group)
+        deq.append(oracle.dequantize_bf16sb(c, s_, b, group))
+    x = W.generic_act((m, 24), (m, d), "f16")
+    r = W.generic_act((m, 25), (m, d), "f16")
+    xd, rd = to_device(x), to_device(r)
+    h = qdm.gemv_gate_up_swiglu(xd, gu)
+    y = qdm.mlp_decode(xd, rd, gu, dn)
+    torch.cuda.synchronize()
+    h_ref, y_ref = oracle.mlp_decode(x.values, r.values, *deq)
+    assert oracle.scaled_error(from_device(h), h_ref) <= H_TOL
+    assert oracle.scaled_error(from_device(y), y_ref) <= TOL["f16"]
+
+
+def test_prefill_mxfp8_rows():
+    qdm = _qdm()
+    m, d, ffn = 100, 1024, 1536
+    print(f"[prefill] m={m} mxfp8", flush=True)
+    fmt = qdm.QDM_MXFP8
+    g32, u32 = W.generic_weights((m, 31), ffn, d), W.generic_weights((m, 32), ffn, d)
+    d32 = W.generic_weights((m, 33), d, ffn)
+    q, e = qdm.quantize_mx_gate_up(g32, u32, fmt)
+    gu = qdm.Weight.from_host(ffn, d, fmt, 32, q, None, block_scales=e)
+    dq, de = qdm.quantize_mx(d32, fmt)
+    dn = qdm.Weight.from_host(d, ffn, fmt, 32, dq, None, block_scales=de)
+    deq = [oracle.dequantize_mx(*oracle.quantize_mx(a, "mxfp8"), "mxfp8") for a in (g32, u32, d32)]
+    x = W.generic_act((m, 34), (m, d), "bf16")
+    r = W.generic_act((m, 35), (m, d), "bf16")
+    xd = to_device(x)
+    h = qdm.gemv_gate_up_swiglu(xd, gu)
+    y = qdm.mlp_decode(xd, to_device(r), gu, dn)
+    torch.cuda.synchronize()
+    h_ref, y_ref = oracle.mlp_decode(x.values, r.values, *deq)
+    assert oracle.scaled_error(from_device(h), h_ref) <= H_TOL
     assert oracle.scaled_error(from_device(y), y_ref) <= TOL["bf16"]
