@@ -23,8 +23,8 @@
  *   - Pointers named "device" are device (HBM) addresses owned by the
  *     caller; "host" pointers are ordinary host memory owned by the caller.
  *     The library's only device allocation and only global state is the
- *     scratch of the few-row down projection (see qdm_gemv_down_residual);
- *     calls are thread-safe.
+ *     split-K partials scratch of the multi-row kernels (see
+ *     qdm_gemv_down_residual); calls are thread-safe.
  *   - GPU work is enqueued on `stream` (a hipStream_t; NULL = the legacy
  *     default stream) and the call returns without waiting.  A failed
  *     launch returns QDM_ERR_HIP.
@@ -209,9 +209,15 @@ int qdm_pack_dense_gate_up(const uint16_t* gate_bf16, const uint16_t* up_bf16,
  * Supported combinations (anything else returns QDM_ERR_UNSUPPORTED):
  *   act     QDM_F32, QDM_BF16 or QDM_F16: the dtype of x, r and out.
  *   weights bits 8 or 4 with group 32/64/128, or bits 16 (dense bf16).
- *   m       1..4096 rows.  Up to 16 rows run in one pass of the kernels; more
- *           rows run as passes of 16 (each pass streams the weights again:
- *           a functional form of multi-row prefill, not a tiled GEMM).
+ *   m       1..4096 rows.  Up to 16 rows run in one pass of the kernels.
+ *           More rows run on tiled dual-GEMM kernels (64 rows per weight
+ *           read; meTile docs, "MLX-LM Backend", section "Dispatch Policy":
+ *           multi-row calls take a fused dual-GEMM gate/up with SwiGLU in
+ *           registers) for 8/4-bit affine (either pair storage) and MX
+ *           weights with a 16-bit act dtype, n a multiple of 16 and k a
+ *           multiple of 128 (4-bit codes) or 64 (8-bit codes); otherwise,
+ *           and for qdm_gemv_linear, as passes of 16 rows (each pass
+ *           streams the weights again).
  *   k       a multiple of 16 (bits 8), 32 (bits 4) or 8 (bits 16).
  * Device pointers x, r, out, h, s_out, n_out, a, b, w must be 16-byte aligned. */
 
@@ -228,7 +234,9 @@ int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act,
  *   h     device fp32 [m][ffn];  r, out: device, act dtype, [m][d]
  *   down  descriptor with n = d, k = ffn.   out may not alias h; it may alias r.
  * With 2..16 rows, 8/4-bit weights and a 16-bit act dtype the sum is split
- * along ffn across thread blocks: the partial sums go to a scratch buffer that
+ * along ffn across thread blocks, and so are both projections of more than 16
+ * rows on the tiled kernels when their output tiles alone would not fill the
+ * device (qdm_gemv_gate_up_swiglu too): the partial sums go to a scratch buffer that
  * the library allocates on the device at the first such call and keeps for the
  * process (growing it, after a device-wide synchronize, when a larger call
  * comes).  The allocating call must not be made while a stream is being

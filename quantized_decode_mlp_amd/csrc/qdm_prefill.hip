@@ -67,8 +67,10 @@ constexpr size_t prefill_lds_bytes() {
            2 * static_cast<size_t>(L::NF) * kPBM * 4;
 }
 
+// Gate/up holds one output fragment pair per wave and runs three waves per
+// SIMD (its registers capped to fit); down holds two fragments at two waves.
 template <int BITS, int G, int XDT, bool GU, int ODT, int NO>
-__global__ void __launch_bounds__(kPT)
+__global__ void __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(GU ? 3 : 2)))
 qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, const void* __restrict__ xin,
                    const void* __restrict__ resid, void* __restrict__ out, float* __restrict__ part, int N, int K,
                    int M, int S) {
