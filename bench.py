@@ -184,7 +184,7 @@ def other_configs(samples, only=None):
         copies = int(-(-(2 << 30) // wl.weight_bytes))
         sets = [(qdm.Weight.from_host(wl.ffn, wl.d, wl.bits, wl.group, q, sb),
                  qdm.Weight.from_host(wl.d, wl.ffn, wl.bits, wl.group, dq, dsb)) for _ in range(copies)]
-        for m in ((only[1],) if only else (wl.rows + (128,) if wi == 5 else (1,))):
+        for m in ((only[1],) if only else (wl.rows + (128, 512) if wi == 5 else (1,))):
             x, r = W.activations(wl, m)
             xd, rd = dev(x), dev(r)
             ws = torch.empty(qdm.mlp_workspace_bytes(m, wl.ffn), dtype=torch.uint8, device="cuda")

@@ -20,10 +20,13 @@
 // chunk takes eight of them.  So each code load is one contiguous piece per
 // lane and chunk, and no MMA runs on masked lanes.  The codes enter the MMA as
 // exact operands (StepCodes) and each chunk's partial tile P is folded in fp32
-// as scale * P + (bias - scale * off) * X, X the chunk's activation sum.
+// as scale * P + (bias - scale * off) * X, X the chunk's activation sum,
+// which one more MMA per row tile and step computes against an all-ones
+// operand (it lands in the accumulator layout of the fold, and the matrix
+// cores have room where the vector units have none).
 //
-// Pipeline.  The activation k-block is staged in one of two LDS buffers (with
-// the chunk sums) while the other is computed on, one barrier per k-block;
+// Pipeline.  The activation k-block is staged in one of two LDS buffers
+// while the other is computed on, one barrier per k-block;
 // activation loads run one k-block ahead in registers, weight loads two.
 //
 // Split K.  When the output tiles alone do not fill the chip, the k-blocks
@@ -58,19 +61,17 @@ struct TileLayout {
     static_assert(LB == 4 || LB == 8 || LB == 16, "chunk piece size");
 };
 
-// Dynamic LDS: two buffers of NH staged parts [64][KBK + pad] (16-bit), then
-// two buffers of chunk sums [NF][64].
+// Dynamic LDS: two buffers of NH staged parts [64][KBK + pad] (16-bit).
 template <int BITS, int G, bool GU>
 constexpr size_t prefill_lds_bytes() {
     using L = TileLayout<BITS, G>;
-    return 2 * (GU ? 1 : 2) * static_cast<size_t>(kPBM) * (L::KBK + kPad) * 2 +
-           2 * static_cast<size_t>(L::NF) * kPBM * 4;
+    return 2 * (GU ? 1 : 2) * static_cast<size_t>(kPBM) * (L::KBK + kPad) * 2;
 }
 
-// Gate/up holds one output fragment pair per wave and runs three waves per
-// SIMD (its registers capped to fit); down holds two fragments at two waves.
+// Gate/up holds one output fragment pair per wave, down two fragments; both
+// run two waves per SIMD.
 template <int BITS, int G, int XDT, bool GU, int ODT, int NO>
-__global__ void __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(GU ? 3 : 2)))
+__global__ void __launch_bounds__(kPT) __attribute__((amdgpu_waves_per_eu(2)))
 qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, const void* __restrict__ xin,
                    const void* __restrict__ resid, void* __restrict__ out, float* __restrict__ part, int N, int K,
                    int M, int S) {
@@ -83,7 +84,6 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
     constexpr int NH = GU ? 1 : 2;            // staged parts: the activations, or h's hi and lo
     constexpr int PPR = KBK / 8;              // 8-element pieces of a staged row
     constexpr int PT = kPBM * PPR / kPT;      // pieces per thread and k-block
-    constexpr int CPF = FG / 8;               // pieces per fold chunk
     constexpr int LDA = KBK + kPad;
     constexpr int XBUF = NH * kPBM * LDA;     // uint16 per staging buffer
     static_assert(PT * kPT == kPBM * PPR, "pieces split evenly");
@@ -91,7 +91,6 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
 
     extern __shared__ __align__(16) uint8_t lds[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
-    float* xsum = reinterpret_cast<float*>(lds + 2 * XBUF * 2);
 
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & 63;
@@ -135,15 +134,13 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
             }
         }
     };
-    // staged in MMA operand order (pairs (e, e + 4) for 4-bit affine codes), with the chunk sums
+    // staged in MMA operand order (pairs (e, e + 4) for 4-bit affine codes)
     auto stage_a = [&](int buf) {
         uint16_t* xb = xs + buf * XBUF;
-        float* xsb = xsum + buf * NF * kPBM;
 #pragma unroll
         for (int j = 0; j < PT; ++j) {
             const int u = tid + j * kPT, row = u / PPR, c = u - row * PPR;
             const bool live = m0 + row < M;
-            float sum = 0.f;
             if constexpr (GU) {
                 const u32x4 v = live ? ax[j] : u32x4{0u, 0u, 0u, 0u};
                 u32x4 o = v;
@@ -153,19 +150,6 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
                         o[i] = __builtin_amdgcn_perm(v[2 + (i >> 1)], v[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
                 }
                 *reinterpret_cast<u32x4*>(xb + row * LDA + c * 8) = o;
-                if constexpr (!MX) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        // the word goes through a scalar: __builtin_bit_cast of a vector
-                        // element expression reinterprets the vector's first element
-                        const uint32_t word = v[i];
-                        if constexpr (XDT == DT_BF16)
-                            sum += __uint_as_float(word << 16) + __uint_as_float(word & 0xffff0000u);
-                        else
-                            sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word),
-                                                         __builtin_bit_cast(h16x2, 0x3c003c00u), sum, false);
-                    }
-                }
             } else {
                 uint32_t hi[8], lo[8];
 #pragma unroll
@@ -173,7 +157,6 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
                     const float v = live ? (e < 4 ? ah[j][0][e] : ah[j][1][e - 4]) : 0.f;
                     hi[e] = __float_as_uint(v) & 0xffff0000u;   // truncation: the exact top half
                     lo[e] = __float_as_uint(v - __uint_as_float(hi[e])) & 0xffff0000u;
-                    sum += __uint_as_float(hi[e]) + __uint_as_float(lo[e]);
                 }
                 u32x4 oh, ol;
 #pragma unroll
@@ -184,11 +167,6 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
                 }
                 *reinterpret_cast<u32x4*>(xb + row * LDA + c * 8) = oh;
                 *reinterpret_cast<u32x4*>(xb + (kPBM + row) * LDA + c * 8) = ol;
-            }
-            if constexpr (!MX) {
-#pragma unroll
-                for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
-                if (c % CPF == 0) xsb[(c / CPF) * kPBM + row] = sum;
             }
         }
     };
@@ -230,14 +208,19 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
     auto compute = [&](int buf, const u32x4 (&cw)[NV], const PairRaw (&pr)[NV][NF]) {
         if (!wlive) return;   // wave-uniform
         const uint16_t* xb = xs + buf * XBUF;
-        const float* xsb = xsum + buf * NF * kPBM;
+        // 1.0 in every element of the operand's 16-bit type: an MMA against it
+        // gives each row's chunk sum X in the accumulator layout the fold uses
+        constexpr uint32_t kOne = MDT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
+        const u32x4 ones = {kOne, kOne, kOne, kOne};
 #pragma unroll
         for (int c = 0; c < NF; ++c) {
-            f32x4 pt[kPA][NV];
+            f32x4 pt[kPA][NV], xc[kPA];
 #pragma unroll
-            for (int a = 0; a < kPA; ++a)
+            for (int a = 0; a < kPA; ++a) {
+                xc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int v = 0; v < NV; ++v) pt[a][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int s = 0; s < SPC; ++s) {
                 const int t = c * SPC + s;
@@ -252,6 +235,7 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
                         const u32x4 av = *reinterpret_cast<const u32x4*>(xb + (hp * kPBM + 16 * a + li) * LDA + ka);
 #pragma unroll
                         for (int v = 0; v < NV; ++v) pt[a][v] = mma<MDT>(av, bv[v], pt[a][v]);
+                        if constexpr (!MX) xc[a] = mma<MDT>(av, ones, xc[a]);
                     }
                 }
             }
@@ -276,10 +260,9 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
 #pragma unroll
                         for (int e = 0; e < 4; ++e) acc[a][v][e] = fmaf(se, pt[a][v][e], acc[a][v][e]);
                     } else {
-                        const f32x4 xc = *reinterpret_cast<const f32x4*>(xsb + c * kPBM + 16 * a + 4 * kq);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            acc[a][v][e] = fmaf(se, pt[a][v][e], fmaf(be, xc[e], acc[a][v][e]));
+                            acc[a][v][e] = fmaf(se, pt[a][v][e], fmaf(be, xc[a][e], acc[a][v][e]));
                     }
                 }
             }
