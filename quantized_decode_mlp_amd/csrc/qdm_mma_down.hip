@@ -85,7 +85,6 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
 
     using Words = typename L::Words;
     Words st[U];
-    const int nflat = rounds * nkw;
 
     f32x4 pw[NPL];
     auto load_pairs = [&](int i) {
@@ -123,12 +122,13 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
         const float x = (gl & 1) ? q4[2] : q4[0], y = (gl & 1) ? q4[3] : q4[1];
         return f32x2{__shfl(x, src, 64), __shfl(y, src, 64)};
     };
-    auto issue = [&](Words& c, int f) {
-        const int i = f / nkw, j = f - i * nkw;
-        const int tile = t0 + i * GP;
-        if (tile >= ntiles) return;   // wave-uniform
+    // code loads of k-block j (clamped to the range) of the wave's tile of round
+    // i (clamped to the last tile): issued on every path, so the compiler can
+    // count them and wait only for the oldest
+    auto issue = [&](Words& c, int i, int j) {
+        const int tile = min(t0 + i * GP, ntiles - 1);
         const uint8_t* qrow = q + static_cast<size_t>(tile * kRows + li) * rb;
-        const int kb0 = k0w + j * KBK;
+        const int kb0 = k0w + min(j, nkw - 1) * KBK;
         if constexpr (WIDE) {
             c = *reinterpret_cast<const Words*>(qrow + static_cast<uint32_t>(kb0 + L::LK * kq) * L::CB / 8);
         } else {
@@ -140,10 +140,6 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
         }
     };
 
-    load_pairs(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        if (u < nflat) issue(st[u], u);
 
     // stage h[:, slice] as bf16 hi + lo (operand order for 4-bit codes) and the
     // fold-chunk sums of hi + lo; sums of rows past m are zero
@@ -192,10 +188,7 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool arow = li < m_rows;
 
-    auto compute = [&](const Words& cw, int f) {
-        const int i = f / nkw, j = f - i * nkw;
-        if (t0 + i * GP >= ntiles) return;   // wave-uniform
-        if (j == 0 && i > 0) load_pairs(i);
+    auto compute = [&](const Words& cw, int j) {
         const int kl = ks * kw + j * KBK;    // k-block start inside the staged slice
         f32x4 pt[NF];
 #pragma unroll
@@ -253,16 +246,21 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    for (int f0 = 0; f0 < nflat; f0 += U) {
+    // per round (one tile): its pairs, then its k-blocks with U code loads in
+    // flight; compute runs only inside the range, the loads on every path
+    for (int i = 0; i < rounds; ++i) {   // uniform per block
+        const bool live = t0 + i * GP < ntiles;   // wave-uniform
+        if (live) load_pairs(i);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int f = f0 + u;
-            if (f < nflat) {
-                compute(st[u], f);
-                if (f + U < nflat) issue(st[u], f + U);
-                if ((f + 1) % nkw == 0) combine(f / nkw);
+        for (int u = 0; u < U; ++u) issue(st[u], i, u);
+        for (int j0 = 0; j0 < nkw; j0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (live && j0 + u < nkw) compute(st[u], j0 + u);
+                issue(st[u], i, j0 + u + U);
             }
         }
+        combine(i);
     }
 }
 
@@ -342,7 +340,7 @@ float* partials_scratch(size_t bytes, void* stream, int& err) {
             err = static_cast<int>(e);
             return nullptr;
         }
-        hipFree(b.first);
+        (void)hipFree(b.first);   // the device has drained; a failure here leaves nothing to undo
         b = {nullptr, 0};
     }
     void* p = nullptr;
@@ -360,7 +358,7 @@ namespace {
 template <int BITS, int G, int ODT>
 int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* r_copy) {
     constexpr int NT = 64 * kDS * kDP;
-    constexpr int U = BlockLayout<BITS, G>::KBK == 128 ? kDU / 2 : kDU;
+    constexpr int U = kDU;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return static_cast<int>(hipErrorInvalidDevice);

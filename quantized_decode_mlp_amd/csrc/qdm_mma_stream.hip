@@ -116,22 +116,24 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         Words c[2];   // [gate, up]: the lane's codes of one k-block
     };
     Stage st[U];
-    const int nflat = rounds * nkw;
 
     // Scale/bias pairs of the wave's groups for one tile, 16 bytes a lane:
     // register r of lane (row li, slot kq) holds groups gbase + 8r + 2kq, +1;
     // a fold chunk takes its pair from lane li + 16 * slot with a shuffle.
+    // Loads are issued on every path (tile, k-block and group clamped to the
+    // range; what a clamped load brings is never used): the compiler can then
+    // count them and wait only for the oldest, where a load on some paths only
+    // turns every wait into a full drain.
     f32x4 pw[2][NPL];
     auto load_pairs = [&](int i) {
-        const int tile = t0 + i * GP;
-        if (tile >= ntiles) return;   // wave-uniform
+        const int tile = min(t0 + i * GP, ntiles - 1);
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
             const size_t row = 2u * static_cast<uint32_t>(tile * kRows + li) + v;
 #pragma unroll
             for (int r = 0; r < NPL; ++r) {
-                const int g = 8 * r + 2 * kq;
-                if (g < gw) {
+                const int g = 8 * r + 2 * kq < gw ? 8 * r + 2 * kq : 0;
+                {
                     if constexpr (mx_bits(BITS)) {
                         // MX: the two blocks' E8M0 bytes as (scale, 0) pairs
                         const uint8_t* e = reinterpret_cast<const uint8_t*>(sb) + row * ngroups + gbase + g;
@@ -161,12 +163,10 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         return f32x2{__shfl(x, src, 64), __shfl(y, src, 64)};
     };
 
-    // loads of flat step f (round f / nkw, k-block f % nkw)
-    auto issue = [&](Stage& s, int f) {
-        const int i = f / nkw, j = f - i * nkw;
-        const int tile = t0 + i * GP;
-        if (tile >= ntiles) return;   // wave-uniform
-        const int kb = ks * nkw + j;
+    // loads of k-block j of round i's tile
+    auto issue = [&](Stage& s, int i, int j) {
+        const int tile = min(t0 + i * GP, ntiles - 1);
+        const int kb = ks * nkw + min(j, nkw - 1);
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
             const uint32_t row = 2u * static_cast<uint32_t>(tile * kRows + li) + v;
@@ -186,8 +186,7 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
 
     load_pairs(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-        if (u < nflat) issue(st[u], u);
+    for (int u = 0; u < U; ++u) issue(st[u], 0, u);
 
     // Stage the rows in LDS as they are (operand order for 4-bit codes) with
     // the fp32 sum of each fold chunk: a piece's sum, then the sum over the
@@ -303,10 +302,7 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     const bool arow = li < m_rows;   // this lane's A row is live
 
-    auto compute = [&](const Stage& s, int f) {
-        const int i = f / nkw, j = f - i * nkw;
-        if (t0 + i * GP >= ntiles) return;   // wave-uniform
-        if (j == 0 && i > 0) load_pairs(i);
+    auto compute = [&](const Stage& s, int j) {
         const int kb = ks * nkw + j;
         // one partial tile per fold chunk; a wide k-block spanning NF groups runs
         // every step once per chunk with the activation kept only on the lanes
@@ -389,18 +385,24 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    // flat pipeline over (round, k-block): U in flight, the tile's partials
-    // combined after its last k-block
-    for (int f0 = 0; f0 < nflat; f0 += U) {
+    // per round (one tile): its pairs and first U k-blocks (round 0's went out
+    // before the staging), then its k-blocks with U in flight, then the
+    // combine; compute runs only inside the range, the loads on every path
+    for (int i = 0; i < rounds; ++i) {   // uniform per block
+        const bool live = t0 + i * GP < ntiles;   // wave-uniform
+        if (i > 0) {
+            load_pairs(i);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int f = f0 + u;
-            if (f < nflat) {
-                compute(st[u], f);
-                if (f + U < nflat) issue(st[u], f + U);
-                if ((f + 1) % nkw == 0) combine(f / nkw);
+            for (int u = 0; u < U; ++u) issue(st[u], i, u);
+        }
+        for (int j0 = 0; j0 < nkw; j0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (live && j0 + u < nkw) compute(st[u], j0 + u);
+                issue(st[u], i, j0 + u + U);
             }
         }
+        combine(i);
     }
 }
 
