@@ -198,3 +198,15 @@ def test_prefill_mxfp8_rows():
     h_ref, y_ref = oracle.mlp_decode(x.values, r.values, *deq)
     assert oracle.scaled_error(from_device(h), h_ref) <= H_TOL
     assert oracle.scaled_error(from_device(y), y_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("bits,group", [(8, 32), (4, 64)])
+def test_prefill_fp32_rows_run_in_passes(bits, group):
+    """fp32 activations: the tiled kernels take 16-bit rows only, so 20 fp32
+    rows run as two passes of the few-row kernels; fp32 bars (1e-5) apply."""
+    m, d, ffn = 20, 512, 1024
+    print(f"[prefill] m={m} f32 bits={bits} group={group}", flush=True)
+    ow, pw = generic_case((m, bits, group, 11), d, ffn, bits, group)
+    x = W.generic_act((m, 1), (m, d), "f32")
+    r = W.generic_act((m, 2), (m, d), "f32")
+    _check(ow, pw, x, r, "f32")
