@@ -179,19 +179,36 @@ __device__ __forceinline__ float e8m0_value(uint32_t e) { return __uint_as_float
 // holds the LK = KBK/4 consecutive k from LK*kq (one 16-byte load per row),
 // k-step t takes its codes 8t .. 8t+7; a block spanning NF > 1 groups runs
 // each step once per group with the activation kept only on that group's
-// lanes.  Otherwise (32-wide groups) a k-block is 64 k, lane kq holds k
-// 32t + 8kq .. +7 of step t (one load per step) and each step is one group.
+// lanes.  Otherwise (32-wide groups) lane kq holds k 32t + 8kq .. +7 of step
+// t and each step is one group: 8-bit codes in 64-k blocks, one load per
+// step; 4-bit codes (GROUPED) in 128-k blocks, lane kq loading the whole
+// group kq (16 bytes) and the four lane slots exchanging words before use
+// (transpose_slots), so that slot kq ends up with its eight codes of every
+// group of the block.
 template <int BITS, int G>
 struct BlockLayout {
     static constexpr int CB = code_width(BITS);   // bits per code
     static constexpr bool WIDE = G >= 64;
-    static constexpr int KBK = (CB == 4 && WIDE) ? 128 : 64;
+    static constexpr bool GROUPED = CB == 4 && !WIDE;
+    static constexpr int KBK = CB == 4 ? 128 : 64;
     static constexpr int STEPS = KBK / 32;
     static constexpr int LK = KBK / 4;
     static constexpr int FG = WIDE ? (G < KBK ? G : KBK) : 32;   // fold chunk (k)
     static constexpr int NF = KBK / FG;                           // fold chunks per k-block
-    using Words = typename std::conditional<WIDE || CB == 8, u32x4, u32x2>::type;
+    using Words = typename std::conditional<WIDE || CB == 8 || GROUPED, u32x4, u32x2>::type;
 };
+
+// The four lane slots' words transposed (slots are the wave's 16-lane rows):
+// word t of slot kq becomes word kq of slot t, by one exchange of row pairs
+// (0,1)<->(2,3) and one of rows 0<->1, 2<->3.
+__device__ __forceinline__ u32x4 transpose_slots(const u32x4& w) {
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    const auto a = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return u32x4{c[0], c[1], d[0], d[1]};
+}
 
 __host__ __device__ constexpr size_t round16(size_t v) { return (v + 15) & ~static_cast<size_t>(15); }
 

@@ -131,6 +131,9 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
         const int kb0 = k0w + min(j, nkw - 1) * KBK;
         if constexpr (WIDE) {
             c = *reinterpret_cast<const Words*>(qrow + static_cast<uint32_t>(kb0 + L::LK * kq) * L::CB / 8);
+        } else if constexpr (L::GROUPED) {
+            // the lane's group kq of the block, whole; exchanged at use
+            c = *reinterpret_cast<const Words*>(qrow + static_cast<uint32_t>(kb0 + 32 * kq) * L::CB / 8);
         } else {
 #pragma unroll
             for (int t = 0; t < STEPS; ++t)
@@ -193,13 +196,15 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
         f32x4 pt[NF];
 #pragma unroll
         for (int fc = 0; fc < NF; ++fc) pt[fc] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Words cwx = cw;
+        if constexpr (L::GROUPED) cwx = transpose_slots(cwx);
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
             const int ka = WIDE ? kl + L::LK * kq + 8 * t : kl + 32 * t + 8 * kq;
             const u32x4 z = u32x4{0u, 0u, 0u, 0u};
             const u32x4 ah = arow ? *reinterpret_cast<const u32x4*>(xh + li * ldx + ka) : z;
             const u32x4 al = arow ? *reinterpret_cast<const u32x4*>(xl + li * ldx + ka) : z;
-            const u32x4 b = SC::operand(SC::step(cw, t));
+            const u32x4 b = SC::operand(SC::step(cwx, t));
 #pragma unroll
             for (int fc = 0; fc < NF; ++fc) {
                 if constexpr (!WIDE) {

@@ -174,6 +174,10 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
             if constexpr (WIDE) {
                 const uint32_t k0 = static_cast<uint32_t>(kb * KBK + L::LK * kq);
                 s.c[v] = *reinterpret_cast<const Words*>(qrow + k0 * L::CB / 8);
+            } else if constexpr (L::GROUPED) {
+                // the lane's group kq of the block, whole; exchanged at use
+                const uint32_t k0 = static_cast<uint32_t>(kb * KBK + 32 * kq);
+                s.c[v] = *reinterpret_cast<const Words*>(qrow + k0 * L::CB / 8);
             } else {
 #pragma unroll
                 for (int t = 0; t < STEPS; ++t) {
@@ -310,11 +314,16 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         f32x4 pt[NF][2];
 #pragma unroll
         for (int fc = 0; fc < NF; ++fc) pt[fc][0] = pt[fc][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Words cg = s.c[0], cu = s.c[1];
+        if constexpr (L::GROUPED) {
+            cg = transpose_slots(cg);
+            cu = transpose_slots(cu);
+        }
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
             const int ka = WIDE ? kb * KBK + L::LK * kq + 8 * t : kb * KBK + 32 * t + 8 * kq;
             const u32x4 a = arow ? *reinterpret_cast<const u32x4*>(xs + li * ldx + ka) : u32x4{0u, 0u, 0u, 0u};
-            const u32x4 bg = SC::operand(SC::step(s.c[0], t)), bu = SC::operand(SC::step(s.c[1], t));
+            const u32x4 bg = SC::operand(SC::step(cg, t)), bu = SC::operand(SC::step(cu, t));
 #pragma unroll
             for (int fc = 0; fc < NF; ++fc) {
                 if constexpr (!WIDE) {
@@ -459,7 +468,7 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
     if (mx_bits(w.bits) && w.group != 32) return false;
     if (act != DT_BF16 && act != DT_F16) return false;
     const int cw = code_width(w.bits);
-    const int kbk = (cw == 4 && w.group >= 64) ? 128 : 64;
+    const int kbk = cw == 4 ? 128 : 64;
     if (w.n % kRows != 0 || w.k % (kbk * kS) != 0) return false;
     // each wave's groups: a whole, even number, at most 8 per pair register
     const int gw = w.k / kS / w.group;
