@@ -609,8 +609,11 @@ int run_stream_s(const qdm_weight& w, const void* x, const void* r, void* out, i
 template <int BITS, int XDT, int ODT, bool GU, int EPI, int S>
 int run_stream_s12(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
                    hipStream_t s, const ChainArgs& ch) {
-    return tw == 1 ? run_stream_st<BITS, XDT, ODT, GU, EPI, S, 1>(w, x, r, out, n_out, k, s, ch)
-                   : run_stream_st<BITS, XDT, ODT, GU, EPI, S, 2>(w, x, r, out, n_out, k, s, ch);
+    // splits with up to 5 waves per row use 1 or 2 tiles per wave; anything else
+    // is not instantiated and is refused rather than run short
+    if (tw == 1) return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 1>(w, x, r, out, n_out, k, s, ch);
+    if (tw == 2) return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 2>(w, x, r, out, n_out, k, s, ch);
+    return static_cast<int>(hipErrorInvalidValue);
 }
 
 template <int BITS, int XDT, int ODT, bool GU, int EPI>
