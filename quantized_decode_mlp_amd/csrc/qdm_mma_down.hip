@@ -278,14 +278,15 @@ qmm_down_reduce_kernel(const float* __restrict__ part, const void* __restrict__ 
     if (idx >= m_rows * N) return;
     const size_t stride = static_cast<size_t>(m_rows) * N;
     const float rv = load_elem<ODT>(r, idx);
-    // eight slices' loads in flight at a time, summed in slice order
+    // sixteen slices' loads in flight at a time (one round trip for up to 16
+    // slices), summed in slice order
     float acc = 0.f;
-    for (int s0 = 0; s0 < NS; s0 += 8) {
-        float v[8];
+    for (int s0 = 0; s0 < NS; s0 += 16) {
+        float v[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = s0 + j < NS ? part[(s0 + j) * stride + idx] : 0.f;
+        for (int j = 0; j < 16; ++j) v[j] = part[min(s0 + j, NS - 1) * stride + idx];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc += v[j];
+        for (int j = 0; j < 16; ++j) acc += s0 + j < NS ? v[j] : 0.f;
     }
     store_elem<ODT>(out, idx, rv + acc);
     if (r_copy) store_elem<ODT>(r_copy, idx, rv);   // the residual's copy, when asked (the decode chain's s)

@@ -59,6 +59,10 @@ struct TileLayout {
     static constexpr int SPC = FG / 32;            // MMA steps per chunk
     static constexpr int LB = FG / 4 * CB / 8;     // code bytes per lane and chunk: 4, 8 or 16
     static_assert(LB == 4 || LB == 8 || LB == 16, "chunk piece size");
+    // 4-bit codes in 32-wide groups: lane slot kq loads the whole group kq (16
+    // bytes) and the slots exchange words before the MMAs (transpose_slots),
+    // which gives each slot its chunk pieces of every group
+    static constexpr bool GROUPED = CB == 4 && FG == 32;
 };
 
 // Dynamic LDS: two buffers of NH staged parts [64][KBK + pad] (16-bit).
@@ -176,10 +180,14 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const uint8_t* qrow = q + static_cast<size_t>(wrow[v]) * rb;
+            if constexpr (L::GROUPED)
+                cw[v] = *reinterpret_cast<const u32x4*>(qrow + static_cast<uint32_t>(kb * KBK + 32 * kq) / 2);
 #pragma unroll
             for (int c = 0; c < NF; ++c) {
                 const uint8_t* src = qrow + static_cast<uint32_t>(kb * KBK + c * FG + kq * (FG / 4)) * L::CB / 8;
-                if constexpr (LB == 16) {
+                if constexpr (L::GROUPED) {
+                    // codes loaded whole above
+                } else if constexpr (LB == 16) {
                     cw[v] = *reinterpret_cast<const u32x4*>(src);
                 } else if constexpr (LB == 8) {
                     const u32x2 p = *reinterpret_cast<const u32x2*>(src);
@@ -205,8 +213,11 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[a][v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf, const u32x4 (&cw)[NV], const PairRaw (&pr)[NV][NF]) {
+    auto compute = [&](int buf, const u32x4 (&cwl)[NV], const PairRaw (&pr)[NV][NF]) {
         if (!wlive) return;   // wave-uniform
+        u32x4 cw[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) cw[v] = L::GROUPED ? transpose_slots(cwl[v]) : cwl[v];
         const uint16_t* xb = xs + buf * XBUF;
         // 1.0 in every element of the operand's 16-bit type: an MMA against it
         // gives each row's chunk sum X in the accumulator layout the fold uses
