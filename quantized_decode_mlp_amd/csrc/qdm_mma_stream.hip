@@ -417,19 +417,26 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
 
 // Block shape: S waves along K per tile, P tiles per block, U k-blocks in flight.
 constexpr int kS = 4, kP = 4, kU = 4;
+// Affine 4-bit codes in 32-wide groups keep the most registers live (pairs of
+// 32 groups per wave and fragment, the exchanged code words): two tiles per
+// block, so that a wave may hold 256 registers instead of 128 and nothing
+// spills.
+template <int BITS, int G>
+constexpr int gate_up_tiles() { return (BITS == 4 || BITS == QDM_U4_SB16) && G == 32 ? 2 : kP; }
 
 template <int BITS, int XDT, int G, bool NORM>
 int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s, const NormArgs& na) {
-    constexpr int NT = 64 * kS * kP;
+    constexpr int P = gate_up_tiles<BITS, G>();
+    constexpr int NT = 64 * kS * P;
     constexpr int XPT = 4;
     // the same bytes in flight per wave: four 64-wide or two 128-wide k-blocks
     constexpr int U = BlockLayout<BITS, G>::KBK == 128 ? kU / 2 : kU;
-    auto kern = qmm_gate_up_stream_kernel<BITS, XDT, G, kS, kP, U, XPT, pair_regs<G>(), NORM>;
+    auto kern = qmm_gate_up_stream_kernel<BITS, XDT, G, kS, P, U, XPT, pair_regs<G>(), NORM>;
     const size_t lds = gate_up_lds_bytes<BITS, G>(m, w.k);
     const int res = resident_blocks(kern, NT, lds);
     if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
     const int ntiles = w.n / kRows;
-    const int need = (ntiles + kP - 1) / kP;
+    const int need = (ntiles + P - 1) / P;
     const int blocks = need < res ? need : res;
     // MX: the block scales take the scale/bias argument (the kernel reads bytes)
     const float* sbp = mx_bits(BITS) ? reinterpret_cast<const float*>(w.block_scales) : w.scale_bias;
