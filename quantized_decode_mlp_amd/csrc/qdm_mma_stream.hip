@@ -488,7 +488,8 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
                                                       : gate_up_lds_bytes<4, 128>(m, w.k))
                                    : (w.group == 32 ? gate_up_lds_bytes<8, 32>(m, w.k)
                                                     : gate_up_lds_bytes<8, 64>(m, w.k));
-    const size_t lds = dyn + static_cast<size_t>(kS - 1) * kP * 2 * 64 * 16 + 2 * kRows * 4 + kRows * 4 * 4;
+    const int tiles = (w.bits == 4 || w.bits == QDM_U4_SB16) && w.group == 32 ? gate_up_tiles<4, 32>() : kP;
+    const size_t lds = dyn + static_cast<size_t>(kS - 1) * tiles * 2 * 64 * 16 + 2 * kRows * 4 + kRows * 4 * 4;
     return lds <= kLdsCap;
 }
 
