@@ -24,6 +24,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 16;     // rows of the matrix tile
 constexpr int kPad = 8;       // f16 padding per staged row: 16 bytes, four LDS banks per row
@@ -179,23 +180,22 @@ __device__ __forceinline__ float e8m0_value(uint32_t e) { return __uint_as_float
 // holds the LK = KBK/4 consecutive k from LK*kq (one 16-byte load per row),
 // k-step t takes its codes 8t .. 8t+7; a block spanning NF > 1 groups runs
 // each step once per group with the activation kept only on that group's
-// lanes.  Otherwise (32-wide groups) lane kq holds k 32t + 8kq .. +7 of step
-// t and each step is one group: 8-bit codes in 64-k blocks, one load per
-// step; 4-bit codes (GROUPED) in 128-k blocks, lane kq loading the whole
-// group kq (16 bytes) and the four lane slots exchanging words before use
-// (transpose_slots), so that slot kq ends up with its eight codes of every
-// group of the block.
+// lanes.  Otherwise (32-wide groups, GROUPED) a k-block is 128 k, lane kq
+// holds k 32t + 8kq .. +7 of step t and each step is one group: lane kq
+// loads the whole group kq (16 bytes of 4-bit codes, 32 of 8-bit ones) and
+// the four lane slots exchange words before use (transpose_slots), so that
+// slot kq ends up with its eight codes of every group of the block.
 template <int BITS, int G>
 struct BlockLayout {
     static constexpr int CB = code_width(BITS);   // bits per code
     static constexpr bool WIDE = G >= 64;
-    static constexpr bool GROUPED = CB == 4 && !WIDE;
-    static constexpr int KBK = CB == 4 ? 128 : 64;
+    static constexpr bool GROUPED = !WIDE;
+    static constexpr int KBK = (CB == 4 || GROUPED) ? 128 : 64;
     static constexpr int STEPS = KBK / 32;
     static constexpr int LK = KBK / 4;
     static constexpr int FG = WIDE ? (G < KBK ? G : KBK) : 32;   // fold chunk (k)
     static constexpr int NF = KBK / FG;                           // fold chunks per k-block
-    using Words = typename std::conditional<WIDE || CB == 8 || GROUPED, u32x4, u32x2>::type;
+    using Words = typename std::conditional<GROUPED && CB == 8, u32x8, u32x4>::type;
 };
 
 // The four lane slots' words transposed (slots are the wave's 16-lane rows):
@@ -208,6 +208,14 @@ __device__ __forceinline__ u32x4 transpose_slots(const u32x4& w) {
     const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
     const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
     return u32x4{c[0], c[1], d[0], d[1]};
+}
+
+// 8-bit codes: a step's eight codes are the word pair (2t, 2t + 1), so the
+// even and the odd words are exchanged separately.
+__device__ __forceinline__ u32x8 transpose_slots(const u32x8& w) {
+    const u32x4 e = transpose_slots(u32x4{w[0], w[2], w[4], w[6]});
+    const u32x4 o = transpose_slots(u32x4{w[1], w[3], w[5], w[7]});
+    return u32x8{e[0], o[0], e[1], o[1], e[2], o[2], e[3], o[3]};
 }
 
 __host__ __device__ constexpr size_t round16(size_t v) { return (v + 15) & ~static_cast<size_t>(15); }

@@ -417,12 +417,13 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
 
 // Block shape: S waves along K per tile, P tiles per block, U k-blocks in flight.
 constexpr int kS = 4, kP = 4, kU = 4;
-// Affine codes in 32-wide groups keep the most registers live (pairs of 32
-// groups per wave and fragment) and the most chunk sums in LDS: two tiles per
-// block, so that a wave may hold 256 registers instead of 128 and 16 staged
-// rows of d = 4096 still fit beside the sums and the combine buffer.
+// 32-wide groups keep the most registers live (pairs of 32 groups per wave
+// and fragment, whole-group code words) and, affine, the most chunk sums in
+// LDS: two tiles per block, so that a wave may hold 256 registers instead of
+// 128 and 16 staged rows of d = 4096 still fit beside the sums and the
+// combine buffer.  MXFP4 (byte scales, 16-byte code words) fits four.
 template <int BITS, int G>
-constexpr int gate_up_tiles() { return !mx_bits(BITS) && G == 32 ? 2 : kP; }
+constexpr int gate_up_tiles() { return G == 32 && BITS != QDM_MXFP4 ? 2 : kP; }
 
 template <int BITS, int XDT, int G, bool NORM>
 int run_gate_up(const qdm_weight& w, const void* x, float* h, int m, hipStream_t s, const NormArgs& na) {
@@ -475,7 +476,7 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
     if (mx_bits(w.bits) && w.group != 32) return false;
     if (act != DT_BF16 && act != DT_F16) return false;
     const int cw = code_width(w.bits);
-    const int kbk = cw == 4 ? 128 : 64;
+    const int kbk = (cw == 4 || w.group == 32) ? 128 : 64;
     if (w.n % kRows != 0 || w.k % (kbk * kS) != 0) return false;
     // each wave's groups: a whole, even number, at most 8 per pair register
     const int gw = w.k / kS / w.group;
@@ -488,7 +489,7 @@ bool mma_stream_gate_up_supported(const qdm_weight& w, int m, int act) {
                                                       : gate_up_lds_bytes<4, 128>(m, w.k))
                                    : (w.group == 32 ? gate_up_lds_bytes<8, 32>(m, w.k)
                                                     : gate_up_lds_bytes<8, 64>(m, w.k));
-    const int tiles = !mx_bits(w.bits) && w.group == 32 ? gate_up_tiles<8, 32>() : kP;
+    const int tiles = w.group == 32 && w.bits != QDM_MXFP4 ? gate_up_tiles<8, 32>() : kP;
     const size_t lds = dyn + static_cast<size_t>(kS - 1) * tiles * 2 * 64 * 16 + 2 * kRows * 4 + kRows * 4 * 4;
     return lds <= kLdsCap;
 }
