@@ -215,7 +215,8 @@ int qdm_pack_dense_gate_up(const uint16_t* gate_bf16, const uint16_t* up_bf16,
  *           multi-row calls take a fused dual-GEMM gate/up with SwiGLU in
  *           registers) for 8/4-bit affine (either pair storage) and MX
  *           weights with a 16-bit act dtype, n a multiple of 16 and k a
- *           multiple of 128 (4-bit codes) or 64 (8-bit codes); otherwise,
+ *           multiple of 128 (4-bit codes, or any codes in groups of 32) or 64
+ *           (8-bit codes in wider groups); otherwise,
  *           and for qdm_gemv_linear, as passes of 16 rows (each pass
  *           streams the weights again).
  *   k       a multiple of 16 (bits 8), 32 (bits 4) or 8 (bits 16).

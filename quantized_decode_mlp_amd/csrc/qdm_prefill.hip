@@ -53,16 +53,17 @@ constexpr int kPT = 64 * kPW;     // threads per block
 template <int BITS, int G>
 struct TileLayout {
     static constexpr int CB = code_width(BITS);
-    static constexpr int KBK = CB == 4 ? 128 : 64;
+    static constexpr int KBK = (CB == 4 || G == 32) ? 128 : 64;
     static constexpr int FG = G < KBK ? G : KBK;   // fold chunk
     static constexpr int NF = KBK / FG;
     static constexpr int SPC = FG / 32;            // MMA steps per chunk
     static constexpr int LB = FG / 4 * CB / 8;     // code bytes per lane and chunk: 4, 8 or 16
     static_assert(LB == 4 || LB == 8 || LB == 16, "chunk piece size");
-    // 4-bit codes in 32-wide groups: lane slot kq loads the whole group kq (16
-    // bytes) and the slots exchange words before the MMAs (transpose_slots),
-    // which gives each slot its chunk pieces of every group
-    static constexpr bool GROUPED = CB == 4 && FG == 32;
+    // 32-wide groups: lane slot kq loads the whole group kq (16 bytes of 4-bit
+    // codes, 32 of 8-bit ones) and the slots exchange words before the MMAs
+    // (transpose_slots), which gives each slot its chunk pieces of every group
+    static constexpr bool GROUPED = FG == 32;
+    using Words = typename std::conditional<GROUPED && CB == 8, u32x8, u32x4>::type;
 };
 
 // Dynamic LDS: two buffers of NH staged parts [64][KBK + pad] (16-bit).
@@ -176,12 +177,13 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
     };
 
     // ---- weights: per fragment, the lane's code piece of every chunk and the chunk's pair
-    auto load_b = [&](u32x4 (&cw)[NV], PairRaw (&pr)[NV][NF], int kb) {
+    using Words = typename L::Words;
+    auto load_b = [&](Words (&cw)[NV], PairRaw (&pr)[NV][NF], int kb) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const uint8_t* qrow = q + static_cast<size_t>(wrow[v]) * rb;
             if constexpr (L::GROUPED)
-                cw[v] = *reinterpret_cast<const u32x4*>(qrow + static_cast<uint32_t>(kb * KBK + 32 * kq) / 2);
+                cw[v] = *reinterpret_cast<const Words*>(qrow + static_cast<uint32_t>(kb * KBK + 32 * kq) * L::CB / 8);
 #pragma unroll
             for (int c = 0; c < NF; ++c) {
                 const uint8_t* src = qrow + static_cast<uint32_t>(kb * KBK + c * FG + kq * (FG / 4)) * L::CB / 8;
@@ -213,9 +215,9 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[a][v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf, const u32x4 (&cwl)[NV], const PairRaw (&pr)[NV][NF]) {
+    auto compute = [&](int buf, const Words (&cwl)[NV], const PairRaw (&pr)[NV][NF]) {
         if (!wlive) return;   // wave-uniform
-        u32x4 cw[NV];
+        Words cw[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) cw[v] = L::GROUPED ? transpose_slots(cwl[v]) : cwl[v];
         const uint16_t* xb = xs + buf * XBUF;
@@ -292,14 +294,14 @@ qmm_prefill_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb, 
     // block staged past the slice lands in the buffer nobody reads again.  The
     // loop body is unrolled by two so that every buffer and set index is a
     // constant.
-    u32x4 cw0[NV], cw1[NV];
+    Words cw0[NV], cw1[NV];
     PairRaw pr0[NV][NF], pr1[NV][NF];
     load_b(cw0, pr0, kb0);
     load_a(kb0);
     stage_a(0);
     load_a(kb0 + min(1, nk - 1));
     __syncthreads();
-    auto iter = [&](int i, int buf, const u32x4 (&cw)[NV], const PairRaw (&pr)[NV][NF], u32x4 (&cwn)[NV],
+    auto iter = [&](int i, int buf, const Words (&cw)[NV], const PairRaw (&pr)[NV][NF], Words (&cwn)[NV],
                     PairRaw (&prn)[NV][NF]) {
         stage_a(buf ^ 1);
         load_b(cwn, prn, kb0 + min(i + 1, nk - 1));
@@ -456,7 +458,7 @@ bool prefill_supported(const qdm_weight& w, int m, int act) {
     if (w.group != 32 && w.group != 64 && w.group != 128) return false;
     if (mx_bits(w.bits) && w.group != 32) return false;
     if (act != DT_BF16 && act != DT_F16) return false;
-    const int kbk = code_width(w.bits) == 4 ? 128 : 64;
+    const int kbk = (code_width(w.bits) == 4 || w.group == 32) ? 128 : 64;
     return w.n % 16 == 0 && w.k % kbk == 0;
 }
 
