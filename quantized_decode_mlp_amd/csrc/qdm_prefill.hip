@@ -14,11 +14,13 @@
 // fragment read from LDS feeds all of the wave's weight fragments.
 //
 // Chunked k layout.  The K loop runs over k-blocks of KBK k (16 code bytes per
-// lane and weight fragment); a k-block is NF fold chunks of FG = min(G, KBK)
-// k and every 32-k MMA step lies inside one chunk: in chunk c, lane slot kq
-// (lane / 16) holds the FG/4 consecutive k from c FG + kq FG/4, step s of the
-// chunk takes eight of them.  So each code load is one contiguous piece per
-// lane and chunk, and no MMA runs on masked lanes.  The codes enter the MMA as
+// lane and weight fragment, 32 for 8-bit codes in 32-wide groups); a k-block
+// is NF fold chunks of FG = min(G, KBK) k and every 32-k MMA step lies inside
+// one chunk: in chunk c, lane slot kq (lane / 16) holds the FG/4 consecutive
+// k from c FG + kq FG/4, step s of the chunk takes eight of them.  So each
+// code load is one contiguous piece per lane and chunk (with 32-wide groups,
+// one load of the slot's whole group and an exchange of words between the
+// slots), and no MMA runs on masked lanes.  The codes enter the MMA as
 // exact operands (StepCodes) and each chunk's partial tile P is folded in fp32
 // as scale * P + (bias - scale * off) * X, X the chunk's activation sum,
 // which one more MMA per row tile and step computes against an all-ones
