@@ -150,7 +150,7 @@ def test_prefill_mx_rows():
     assert oracle.scaled_error(from_device(y), y_ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("bits,group", [(8, 128), (4, 64)])
+@pytest.mark.parametrize("bits,group", [(8, 128), (4, 64), (4, 32), (8, 32)])
 def test_prefill_sb16_rows(bits, group):
     qdm = _qdm()
     fmt = {8: qdm.QDM_U8_SB16, 4: qdm.QDM_U4_SB16}[bits]

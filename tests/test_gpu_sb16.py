@@ -72,7 +72,7 @@ def test_sb16_workload_shapes(wl_index):
 
 
 @pytest.mark.parametrize("act", ["bf16", "f16"])
-@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (4, 128), (8, 128)])
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32), (4, 128), (8, 128), (8, 32)])
 @pytest.mark.parametrize("m", [1, 4, 16])
 def test_sb16_rows(m, bits, group, act):
     print(f"[sb16] m={m} bits={bits} group={group} act={act}", flush=True)
