@@ -402,6 +402,30 @@ def projection_configs(samples, dev):
     _log(f"attention q/k/v/o: {med:.2f} us per layer")
     del layers
     torch.cuda.empty_cache()
+
+    # the same projections with q, k and v as one weight (packed rows and their
+    # pairs concatenated: every row is quantized on its own) and o: 2 launches
+    n_qkv = sum(W.PROJECTIONS[k].n for k in keys[:3])
+    qkv_q = np.ascontiguousarray(np.concatenate([prep[j][0] for j in range(3)], axis=0))
+    qkv_sb = np.ascontiguousarray(np.concatenate([prep[j][1] for j in range(3)], axis=0))
+    qkv_b = torch.cat([prep[j][2] for j in range(3)])
+    po = W.PROJECTIONS[keys[3]]
+    fused = [(qdm.Weight.from_host(n_qkv, po.k, po.bits, po.group, qkv_q, qkv_sb),
+              qdm.Weight.from_host(po.n, po.k, po.bits, po.group, prep[3][0], prep[3][1])) for _ in range(copies)]
+    o_qkv = torch.empty((1, n_qkv), dtype=xd.dtype, device="cuda")
+
+    def attn_fused(i):
+        qdm.gemv_linear(xd, fused[i][0], bias=qkv_b, out=o_qkv)
+        qdm.gemv_linear(xd, fused[i][1], bias=prep[3][2], out=outs[3])
+
+    t = graph_samples(attn_fused, copies, samples)
+    med = float(np.median(t))
+    res["attention_fused_qkv_o_qwen25_1p5b"] = {"us_per_layer": pcts(t), "launches": 2,
+                                                "weight_GBps": round(layer_bytes / (med * 1e-6) / 1e9, 1),
+                                                "copies": copies}
+    _log(f"attention fused qkv + o: {med:.2f} us per layer")
+    del fused
+    torch.cuda.empty_cache()
     return res
 
 
