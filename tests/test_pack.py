@@ -209,3 +209,15 @@ def test_sb16_rejects():
     w[0, 1] = np.inf
     assert L.qdm_quantize_pack_rows_sb16(q._ptr(w), 2, 64, 8, 32, q._ptr(qb), q._ptr(sb)) == q.QDM_ERR_INVALID_ARG
     assert q.packed_q_bytes(4, 64, q.QDM_U4_SB16) == 128 and q.packed_q_bytes(4, 64, q.QDM_U8_SB16) == 256
+
+
+@pytest.mark.parametrize("bits,group", [(8, 32), (4, 64)])
+def test_stacked_rows_pack_as_concatenation(bits, group):
+    """Rows are quantized one by one, so the packing of stacked matrices (a
+    fused q/k/v weight) is the concatenation of their packings, bytes and
+    (scale, bias) pairs alike."""
+    mats = [W.generic_weights((bits, group, i), n, 256, 0.02) for i, n in enumerate((48, 16, 16))]
+    parts = [q.quantize_pack_rows(a, bits, group) for a in mats]
+    codes, sb = q.quantize_pack_rows(np.concatenate(mats), bits, group)
+    assert np.array_equal(codes, np.concatenate([p[0] for p in parts]))
+    assert np.array_equal(sb, np.concatenate([p[1] for p in parts]))
