@@ -210,3 +210,17 @@ def test_prefill_fp32_rows_run_in_passes(bits, group):
     x = W.generic_act((m, 1), (m, d), "f32")
     r = W.generic_act((m, 2), (m, d), "f32")
     _check(ow, pw, x, r, "f32")
+
+
+@pytest.mark.parametrize("bits,group,d", [(4, 64, 128), (8, 64, 64), (4, 32, 128), (8, 32, 128)])
+@pytest.mark.parametrize("m", [17, 65])
+def test_prefill_smallest_shapes(m, bits, group, d):
+    """One k-block of K (a pipeline of one iteration, no split), a single
+    block of outputs (at d = 64 the down projection's block has two idle
+    waves), ragged rows."""
+    ffn = 128 if bits == 4 or group == 32 else 64
+    print(f"[prefill] smallest m={m} bits={bits} group={group} d={d} ffn={ffn}", flush=True)
+    ow, pw = generic_case((m, bits, group, d, 13), d, ffn, bits, group)
+    x = W.generic_act((m, 1), (m, d), "bf16")
+    r = W.generic_act((m, 2), (m, d), "bf16")
+    _check(ow, pw, x, r, "bf16")
