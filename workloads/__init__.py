@@ -224,3 +224,74 @@ def generic_weights(seed, n: int, k: int, sigma: float = 0.02) -> np.ndarray:
 def generic_act(seed, shape, dtype: str, sigma: float = 1.0) -> Act:
     a = normal_f32(np.random.default_rng(np.random.SeedSequence(list(seed))), shape, sigma)
     return to_storage(a, dtype)
+
+
+# ---------------------------------------------------------------- edge-case draws
+#
+# Structured inputs for the parity cases that stress the kernels' decoding:
+# groups whose codes sit at the two ends of the range, constant groups,
+# activations of one sign, and activations spanning many binades inside one
+# 16-element run.  These only place values; what the quantizer makes of them
+# is the quantizer's business.
+
+EDGE_WEIGHTS = ("outlier", "constant", "gaussian")
+EDGE_ACTS = ("positive", "wide", "gaussian")
+
+
+def edge_weights(pattern: str, seed, n: int, k: int, group: int, sigma: float = 0.02) -> np.ndarray:
+    """fp32 [n, k] weights by group of ``group`` columns.
+
+    outlier:  every group holds one common value (its minimum, ~ N(0, sigma))
+              in all places but one, which lies above it by |N(0, 5 sigma)| + 2.5 sigma;
+    constant: every other group is constant (a non-zero ~ N(0, sigma) value,
+              pushed away from 0), the others ~ N(0, sigma);
+    gaussian: ~ N(0, sigma)."""
+    if k % group:
+        raise ValueError("k must be a multiple of group")
+    rng = np.random.default_rng(np.random.SeedSequence(list(seed)))
+    ng = k // group
+    if pattern == "gaussian":
+        return normal_f32(rng, (n, k), sigma)
+    if pattern == "outlier":
+        base = normal_f32(rng, (n, ng), sigma)
+        w = np.repeat(base[:, :, None], group, axis=2)
+        pos = rng.integers(0, group, size=(n, ng))
+        lift = (np.abs(normal_f32(rng, (n, ng), 5 * sigma)) + np.float32(2.5 * sigma)).astype(np.float32)
+        rows, cols = np.meshgrid(np.arange(n), np.arange(ng), indexing="ij")
+        w[rows, cols, pos] = base + lift
+        return np.ascontiguousarray(w.reshape(n, k), dtype=np.float32)
+    if pattern == "constant":
+        w = normal_f32(rng, (n, ng, group), sigma)
+        c = normal_f32(rng, (n, ng), sigma)
+        c = np.where(np.abs(c) < sigma / 4, np.float32(sigma / 2), c).astype(np.float32)
+        w[:, 0::2, :] = c[:, 0::2, None]
+        return np.ascontiguousarray(w.reshape(n, k), dtype=np.float32)
+    raise ValueError(f"unknown weight pattern {pattern!r}")
+
+
+def edge_activations(pattern: str, seed, shape, dtype: str) -> Act:
+    """Activations [.., d] in ``dtype``.
+
+    positive: |N(0, 1)|;
+    wide:     random signs, magnitudes (1 + U[0,1)) * 2^e with e uniform in
+              [-14, 2], and in every aligned run of 16 elements the first at
+              (1 + U[0,1)) * 2^6 and the second exactly 2^-14, so each run
+              spans at least 2^20 (all f16 normals; small enough that an MLP's
+              outputs stay inside the f16 range);
+    gaussian: N(0, 1)."""
+    rng = np.random.default_rng(np.random.SeedSequence(list(seed)))
+    if pattern == "gaussian":
+        return to_storage(normal_f32(rng, shape), dtype)
+    if pattern == "positive":
+        return to_storage(np.abs(normal_f32(rng, shape)), dtype)
+    if pattern == "wide":
+        d = shape[-1]
+        if d % 16:
+            raise ValueError("the last dim must be a multiple of 16")
+        e = rng.integers(-14, 3, size=shape)
+        e[..., 0::16] = 6
+        mag = (1.0 + rng.random(size=shape)) * np.exp2(e)
+        mag[..., 1::16] = 2.0 ** -14
+        sign = np.where(rng.random(size=shape) < 0.5, -1.0, 1.0)
+        return to_storage((sign * mag).astype(np.float32), dtype)
+    raise ValueError(f"unknown activation pattern {pattern!r}")
