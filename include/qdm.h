@@ -22,9 +22,12 @@
  *     is launched or written: on error no output byte is touched.
  *   - Pointers named "device" are device (HBM) addresses owned by the
  *     caller; "host" pointers are ordinary host memory owned by the caller.
- *     The library's only device allocation and only global state is the
- *     split-K partials scratch of the multi-row kernels (see
- *     qdm_gemv_down_residual); calls are thread-safe.
+ *     The library allocates, frees and synchronizes nothing: every buffer a
+ *     kernel writes, scratch included, is an argument (a workspace sized by
+ *     the matching *_workspace_bytes query), so any call may be captured
+ *     into a HIP graph.  The only state it keeps is a per-device cache of
+ *     occupancy queries.  Calls on different streams are independent when
+ *     their workspaces and outputs are distinct.
  *   - GPU work is enqueued on `stream` (a hipStream_t; NULL = the legacy
  *     default stream) and the call returns without waiting.  A failed
  *     launch returns QDM_ERR_HIP.
@@ -71,7 +74,7 @@ typedef enum qdm_status {
     QDM_ERR_INVALID_ARG = -1,   /* NULL pointer, non-positive or inconsistent size, non-finite weight */
     QDM_ERR_UNSUPPORTED = -2,   /* valid but not provided: bits/group/dtype/row-count combination */
     QDM_ERR_ALIGNMENT = -3,     /* a pointer is not aligned as the entry point requires */
-    QDM_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than qdm_mlp_workspace_bytes() */
+    QDM_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than its *_workspace_bytes() query */
     QDM_ERR_HIP = -5            /* the HIP runtime refused a launch */
 } qdm_status;
 
@@ -121,9 +124,24 @@ size_t qdm_scale_bias_floats(int32_t n, int32_t k, int32_t group);
 /* Bytes of the E8M0 block scales of an MX [n][k] matrix: n*k/32; 0 if invalid. */
 size_t qdm_mx_scale_bytes(int32_t n, int32_t k);
 
-/* Workspace bytes qdm_mlp_decode needs for m rows: the fp32 hidden row(s)
- * h[m][ffn], rounded up to 256 bytes; 0 if invalid. */
-size_t qdm_mlp_workspace_bytes(int32_t m, int32_t ffn);
+/* Workspace sizes.  A projection whose kernel splits the contraction across
+ * thread blocks (2..16 rows of the down projection on the matrix cores; more
+ * than 16 rows on the tiled kernels when their output tiles alone would not
+ * fill the chip) writes fp32 partial sums to the caller's workspace; these
+ * queries give the bytes a call with the same arguments needs, computed from
+ * the shapes and formats only (no device is touched; the tiled kernels' split
+ * is sized for the full 256-CU chip, which bounds any device).  They return 0
+ * for invalid arguments, which the call itself then rejects. */
+
+/* qdm_gemv_gate_up_swiglu: partials only (0 when that call splits nothing). */
+size_t qdm_gemv_gate_up_workspace_bytes(int32_t m, qdm_dtype act, const qdm_weight* gate_up);
+
+/* qdm_gemv_down_residual: partials only (0 when that call splits nothing). */
+size_t qdm_gemv_down_workspace_bytes(int32_t m, qdm_dtype act, const qdm_weight* down);
+
+/* qdm_mlp_decode: the fp32 hidden rows h[m][ffn] (rounded up to 256 bytes),
+ * then the larger of the two projections' partials (rounded up to 256). */
+size_t qdm_mlp_workspace_bytes(int32_t m, qdm_dtype act, const qdm_weight* gate_up, const qdm_weight* down);
 
 /* ----------------------------------------------------------------- host: quantize / pack
  * Ahead-of-time preparation, once per weight set, on host buffers.  The pages
@@ -223,30 +241,34 @@ int qdm_pack_dense_gate_up(const uint16_t* gate_bf16, const uint16_t* up_bf16,
  * Device pointers x, r, out, h, s_out, n_out, a, b, w must be 16-byte aligned. */
 
 /* h[m][ffn] = silu(G) * U with G = x W_gate^T, U = x W_up^T, fp32 accumulation,
- * one write of h (fp32) per element.
- *   x        device, act dtype, [m][d]
- *   gate_up  interleaved pair descriptor (n = ffn, k = d)
- *   h_out    device fp32 [m][ffn]                                            */
-int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act,
-                            const qdm_weight* gate_up, float* h_out, void* stream);
+ * one write of h (fp32) per element.  Defined by "Compute-Graph Fusion",
+ * section "Automatic Gated Epilogues" (two projections over one activation,
+ * silu(gate) * up applied on chip) and "MLX-LM Backend", section "Dispatch
+ * Policy" (gate and up share each activation load; the SwiGLU epilogue
+ * precedes the only write of the hidden tile).
+ *   x          device, act dtype, [m][d]
+ *   gate_up    interleaved pair descriptor (n = ffn, k = d)
+ *   workspace  device, >= qdm_gemv_gate_up_workspace_bytes(m, act, gate_up)
+ *              bytes, 16-byte aligned; may be NULL when that is 0
+ *   h_out      device fp32 [m][ffn]
+ * x, h_out and the workspace must not overlap (INVALID_ARG).               */
+int qdm_gemv_gate_up_swiglu(const void* x, int32_t m, qdm_dtype act, const qdm_weight* gate_up,
+                            void* workspace, size_t workspace_bytes, float* h_out, void* stream);
 
 /* out[m][d] = r + h W_down^T, fp32 accumulation, the residual added in fp32 and
- * the sum rounded once (nearest-even) to the act dtype.
- *   h     device fp32 [m][ffn];  r, out: device, act dtype, [m][d]
- *   down  descriptor with n = d, k = ffn.   out may not alias h; it may alias r.
- * With 2..16 rows, 8/4-bit weights and a 16-bit act dtype the sum is split
- * along ffn across thread blocks, and so are both projections of more than 16
- * rows on the tiled kernels when their output tiles alone would not fill the
- * device (qdm_gemv_gate_up_swiglu too): the partial sums go to a scratch buffer that
- * the library allocates on the device at the first such call and keeps for the
- * process (growing it, after a device-wide synchronize, when a larger call
- * comes).  The allocating call must not be made while a stream is being
- * captured into a graph (it then returns QDM_ERR_HIP): warm the largest shape
- * up first.  All streams of a device share the buffer, so such calls that
- * could run at the same time on different streams of one device must be
- * ordered by the caller. */
-int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype act,
-                           const qdm_weight* down, void* out, void* stream);
+ * the sum rounded once (nearest-even) to the act dtype.  Defined by
+ * "Compute-Graph Fusion", section "Automatic Gated Epilogues" (for one-row
+ * decode the transformer residual is added inside the down projection) and
+ * "MLX-LM Backend", section "Dispatch Policy" (the typed store adds the
+ * residual without materializing the projection's own result).
+ *   h          device fp32 [m][ffn];  r, out: device, act dtype, [m][d]
+ *   down       descriptor with n = d, k = ffn
+ *   workspace  device, >= qdm_gemv_down_workspace_bytes(m, act, down) bytes,
+ *              16-byte aligned; may be NULL when that is 0
+ * out may alias r; out must not overlap h, and the workspace none of h, r,
+ * out (INVALID_ARG). */
+int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype act, const qdm_weight* down,
+                           void* workspace, size_t workspace_bytes, void* out, void* stream);
 
 /* out[m][n] = x W^T + bias, fp32 accumulation, bias added in fp32, the sum
  * rounded once (nearest-even) to the act dtype.  The one-row decode
@@ -259,22 +281,29 @@ int qdm_gemv_down_residual(const float* h, const void* r, int32_t m, qdm_dtype a
  *   w     descriptor [n][k]: bits 8/4 with group 32/64/128, or 16 (dense
  *         bf16); a tied embedding is the [vocab][d] table itself (n = vocab).
  *   bias  device, act dtype, [n], shared by the m rows; NULL for none.
- *   out   device, act dtype, [m][n]; may alias neither x nor bias.
+ *   out   device, act dtype, [m][n]; may overlap neither x nor bias.
  * One row runs on the weight-streaming kernel; 2..16 rows on the vector
  * kernel four rows a pass. */
 int qdm_gemv_linear(const void* x, int32_t m, qdm_dtype act, const qdm_weight* w, const void* bias, void* out,
                     void* stream);
 
-/* The whole MLP: the two launches above on one stream, h kept in `workspace`
- * (device, >= qdm_mlp_workspace_bytes(m, ffn) bytes, 16-byte aligned).
+/* The whole MLP, out = r + W_down (silu(W_gate x) * (W_up x)): the two
+ * projections above on one stream ("Compute-Graph Fusion", "Automatic Gated
+ * Epilogues": the gated pair, then the down projection with the residual).
+ *   x, r, out  device, act dtype, [m][d]; out may alias x or r
+ *   workspace  device, >= qdm_mlp_workspace_bytes(m, act, gate_up, down)
+ *              bytes, 16-byte aligned, overlapping none of x, r, out
+ *              (INVALID_ARG): h, then the projections' partial sums
  * gate_up->k must equal down->n (= d) and gate_up->n must equal down->k (= ffn);
- * both descriptors must use the same bits.  The down half keeps its partial
- * sums in the library's device scratch as qdm_gemv_down_residual does. */
+ * both descriptors must use the same bits. */
 int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
                    const qdm_weight* gate_up, const qdm_weight* down,
                    void* workspace, size_t workspace_bytes, void* out, void* stream);
 
-/* Residual add + RMSNorm with both outputs, per row:
+/* Residual add + RMSNorm with both outputs, per row ("Compute-Graph Fusion",
+ * the opening GraphBuilder example: the add feeds RMSNorm and the sum stays a
+ * second output of one kernel; "MLX-LM Backend", "Dispatch Policy": RMSNorm
+ * accumulates in FP32):
  *   s = a + b rounded once to `dtype`;  n = s * w / sqrt(mean(s^2) + eps)
  * with fp32 accumulation of the mean square; n rounded once to `dtype`.
  *   a, b, s_out, n_out: device, dtype, [rows][n];  w: device, dtype, [n]
@@ -282,9 +311,10 @@ int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
 int qdm_add_rmsnorm(const void* a, const void* b, const void* w, int32_t rows, int32_t n,
                     float eps, qdm_dtype dtype, void* s_out, void* n_out, void* stream);
 
-/* Workspace bytes qdm_mlp_decode_rmsnorm needs: h[m][ffn] fp32 plus two
- * [m][d] rows of the act dtype, each rounded up to 256 bytes; 0 if invalid. */
-size_t qdm_mlp_rmsnorm_workspace_bytes(int32_t m, int32_t d, int32_t ffn, qdm_dtype act);
+/* Workspace bytes qdm_mlp_decode_rmsnorm needs: h[m][ffn] fp32, two [m][d]
+ * rows of the act dtype, then the projections' partial sums, each part
+ * rounded up to 256 bytes; 0 if invalid. */
+size_t qdm_mlp_rmsnorm_workspace_bytes(int32_t m, qdm_dtype act, const qdm_weight* gate_up, const qdm_weight* down);
 
 /* The decode chain across the layer boundary: the residual add + RMSNorm
  * above feeding the MLP, with the sum as the MLP's residual ("Compute-Graph
@@ -298,15 +328,15 @@ size_t qdm_mlp_rmsnorm_workspace_bytes(int32_t m, int32_t d, int32_t ffn, qdm_dt
  * square and n from a, b and w, and the down launch adds s as its residual
  * (n and s never go to HBM).  With 2..16 rows on the matrix-core kernels
  * every gate/up block rebuilds n likewise and s goes through the workspace
- * to the down projection (which then uses the device scratch described at
- * qdm_gemv_down_residual).  Otherwise the three launches run in order
+ * to the down projection.  Otherwise the three launches run in order
  * through the workspace.
  *   a, b     device, act dtype, [m][d]; out may alias either.
  *   norm_w   device, act dtype, [d];  eps >= 0 and finite.
  *   s_out    device, act dtype, [m][d], or NULL (s not written); may alias
  *            a or b, not out.
- *   workspace device, >= qdm_mlp_rmsnorm_workspace_bytes(m, d, ffn, act)
- *            bytes, 16-byte aligned, overlapping no other argument.
+ *   workspace device, >= qdm_mlp_rmsnorm_workspace_bytes(m, act, gate_up,
+ *            down) bytes, 16-byte aligned, overlapping none of a, b, norm_w,
+ *            s_out, out (INVALID_ARG).
  *   Weights as for qdm_mlp_decode (gate_up->k = down->n = d, same bits). */
 int qdm_mlp_decode_rmsnorm(const void* a, const void* b, const void* norm_w, float eps, int32_t m, qdm_dtype act,
                            const qdm_weight* gate_up, const qdm_weight* down,

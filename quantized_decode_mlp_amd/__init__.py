@@ -32,6 +32,7 @@ QDM_U4_SB16, QDM_U8_SB16 = 0x204, 0x208   # affine 4/8-bit with bf16 (scale, bia
 # Every symbol include/qdm.h declares (checked by the tests).
 EXPORTS = (
     "qdm_packed_q_bytes", "qdm_scale_bias_floats", "qdm_mlp_workspace_bytes",
+    "qdm_gemv_gate_up_workspace_bytes", "qdm_gemv_down_workspace_bytes",
     "qdm_quantize_affine", "qdm_pack_rows", "qdm_quantize_pack_rows",
     "qdm_quantize_pack_gate_up", "qdm_pack_gate_up", "qdm_pack_dense_gate_up",
     "qdm_gemv_gate_up_swiglu", "qdm_gemv_down_residual", "qdm_gemv_linear", "qdm_mlp_decode",
@@ -64,23 +65,26 @@ def _load():
                           "`python quantized_decode_mlp_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     i32, sz, vp, f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    pw = ctypes.POINTER(qdm_weight)
     sig = {
         "qdm_packed_q_bytes": (sz, [i32, i32, i32]),
         "qdm_scale_bias_floats": (sz, [i32, i32, i32]),
-        "qdm_mlp_workspace_bytes": (sz, [i32, i32]),
+        "qdm_mlp_workspace_bytes": (sz, [i32, ctypes.c_int, pw, pw]),
+        "qdm_gemv_gate_up_workspace_bytes": (sz, [i32, ctypes.c_int, pw]),
+        "qdm_gemv_down_workspace_bytes": (sz, [i32, ctypes.c_int, pw]),
         "qdm_quantize_affine": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp, vp]),
         "qdm_pack_rows": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "qdm_quantize_pack_rows": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp]),
         "qdm_quantize_pack_gate_up": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, vp, vp]),
         "qdm_pack_gate_up": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "qdm_pack_dense_gate_up": (ctypes.c_int, [vp, vp, i32, i32, vp]),
-        "qdm_gemv_gate_up_swiglu": (ctypes.c_int, [vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight), vp, vp]),
-        "qdm_gemv_down_residual": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight), vp, vp]),
+        "qdm_gemv_gate_up_swiglu": (ctypes.c_int, [vp, i32, ctypes.c_int, pw, vp, sz, vp, vp]),
+        "qdm_gemv_down_residual": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, pw, vp, sz, vp, vp]),
         "qdm_gemv_linear": (ctypes.c_int, [vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight), vp, vp, vp]),
         "qdm_mlp_decode": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
                                           ctypes.POINTER(qdm_weight), vp, sz, vp, vp]),
         "qdm_add_rmsnorm": (ctypes.c_int, [vp, vp, vp, i32, i32, f32, ctypes.c_int, vp, vp, vp]),
-        "qdm_mlp_rmsnorm_workspace_bytes": (sz, [i32, i32, i32, ctypes.c_int]),
+        "qdm_mlp_rmsnorm_workspace_bytes": (sz, [i32, ctypes.c_int, pw, pw]),
         "qdm_mlp_decode_rmsnorm": (ctypes.c_int, [vp, vp, vp, f32, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
                                                   ctypes.POINTER(qdm_weight), vp, sz, vp, vp, vp]),
         "qdm_mx_scale_bytes": (sz, [i32, i32]),
@@ -123,12 +127,21 @@ def scale_bias_floats(n: int, k: int, group: int) -> int:
     return int(_lib.qdm_scale_bias_floats(n, k, group))
 
 
-def mlp_workspace_bytes(m: int, ffn: int) -> int:
-    return int(_lib.qdm_mlp_workspace_bytes(m, ffn))
+def mlp_workspace_bytes(m: int, act: int, gate_up: "Weight", down: "Weight") -> int:
+    return int(_lib.qdm_mlp_workspace_bytes(m, act, ctypes.byref(gate_up.descriptor), ctypes.byref(down.descriptor)))
 
 
-def mlp_rmsnorm_workspace_bytes(m: int, d: int, ffn: int, dtype: int) -> int:
-    return int(_lib.qdm_mlp_rmsnorm_workspace_bytes(m, d, ffn, dtype))
+def mlp_rmsnorm_workspace_bytes(m: int, act: int, gate_up: "Weight", down: "Weight") -> int:
+    return int(_lib.qdm_mlp_rmsnorm_workspace_bytes(m, act, ctypes.byref(gate_up.descriptor),
+                                                    ctypes.byref(down.descriptor)))
+
+
+def gemv_gate_up_workspace_bytes(m: int, act: int, gate_up: "Weight") -> int:
+    return int(_lib.qdm_gemv_gate_up_workspace_bytes(m, act, ctypes.byref(gate_up.descriptor)))
+
+
+def gemv_down_workspace_bytes(m: int, act: int, down: "Weight") -> int:
+    return int(_lib.qdm_gemv_down_workspace_bytes(m, act, ctypes.byref(down.descriptor)))
 
 
 # ------------------------------------------------------------------ host: quantize / pack
@@ -346,18 +359,29 @@ class Weight:
         return Weight(n, k, bits, group, qt, sbt, bst)
 
 
-def gemv_gate_up_swiglu(x, gate_up: Weight, h_out=None, stream=None):
+def _workspace(workspace, nbytes, device):
+    """(pointer, bytes) of a caller's workspace, or of a new one when none is
+    given and nbytes > 0; (None, 0) when none is needed."""
+    if workspace is None:
+        if nbytes == 0:
+            return None, 0
+        workspace = _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def gemv_gate_up_swiglu(x, gate_up: Weight, h_out=None, workspace=None, stream=None):
     """x [m, d] (f32/f16/bf16, device) -> h [m, ffn] fp32."""
     torch = _torch()
     m = x.shape[0] if x.dim() == 2 else 1
     if h_out is None:
         h_out = torch.empty((m, gate_up.n), dtype=torch.float32, device=x.device)
-    _check(_lib.qdm_gemv_gate_up_swiglu(_dev(x, "x"), m, _dt(x), ctypes.byref(gate_up.descriptor),
+    ws, nbytes = _workspace(workspace, gemv_gate_up_workspace_bytes(m, _dt(x), gate_up), x.device)
+    _check(_lib.qdm_gemv_gate_up_swiglu(_dev(x, "x"), m, _dt(x), ctypes.byref(gate_up.descriptor), ws, nbytes,
                                         _dev(h_out, "h_out"), _stream(stream)), "qdm_gemv_gate_up_swiglu")
     return h_out
 
 
-def gemv_down_residual(h, r, down: Weight, out=None, stream=None):
+def gemv_down_residual(h, r, down: Weight, out=None, workspace=None, stream=None):
     """h [m, ffn] fp32, r [m, d] -> out [m, d] (dtype of r)."""
     torch = _torch()
     m = r.shape[0] if r.dim() == 2 else 1
@@ -365,8 +389,9 @@ def gemv_down_residual(h, r, down: Weight, out=None, stream=None):
         out = torch.empty_like(r)
     if out.dtype != r.dtype:
         raise TypeError("out must have the dtype of r")
-    _check(_lib.qdm_gemv_down_residual(_dev(h, "h"), _dev(r, "r"), m, _dt(r), ctypes.byref(down.descriptor),
-                                       _dev(out, "out"), _stream(stream)), "qdm_gemv_down_residual")
+    ws, nbytes = _workspace(workspace, gemv_down_workspace_bytes(m, _dt(r), down), r.device)
+    _check(_lib.qdm_gemv_down_residual(_dev(h, "h"), _dev(r, "r"), m, _dt(r), ctypes.byref(down.descriptor), ws,
+                                       nbytes, _dev(out, "out"), _stream(stream)), "qdm_gemv_down_residual")
     return out
 
 
@@ -390,17 +415,14 @@ def mlp_decode(x, r, gate_up: Weight, down: Weight, workspace=None, out=None, st
     m = x.shape[0] if x.dim() == 2 else 1
     if x.dtype != r.dtype:
         raise TypeError("x and r must share a dtype")
-    ws_bytes = mlp_workspace_bytes(m, gate_up.n)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty_like(r)
     if out.dtype != r.dtype:
         raise TypeError("out must have the dtype of r")
-    nbytes = workspace.numel() * workspace.element_size()
+    ws, nbytes = _workspace(workspace, mlp_workspace_bytes(m, _dt(x), gate_up, down), x.device)
     _check(_lib.qdm_mlp_decode(_dev(x, "x"), _dev(r, "r"), m, _dt(x), ctypes.byref(gate_up.descriptor),
-                               ctypes.byref(down.descriptor), _dev(workspace, "workspace"), nbytes,
-                               _dev(out, "out"), _stream(stream)), "qdm_mlp_decode")
+                               ctypes.byref(down.descriptor), ws, nbytes, _dev(out, "out"), _stream(stream)),
+           "qdm_mlp_decode")
     return out
 
 
@@ -427,17 +449,14 @@ def mlp_decode_rmsnorm(a, b, norm_w, eps: float, gate_up: Weight, down: Weight, 
     if not (a.dtype == b.dtype == norm_w.dtype):
         raise TypeError("a, b and norm_w must share a dtype")
     m = a.shape[0] if a.dim() == 2 else 1
-    ws_bytes = mlp_rmsnorm_workspace_bytes(m, gate_up.k, gate_up.n, _dt(a))
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
     if out is None:
         out = torch.empty_like(a)
     if out.dtype != a.dtype or (s_out is not None and s_out.dtype != a.dtype):
         raise TypeError("out and s_out must have the dtype of a")
-    nbytes = workspace.numel() * workspace.element_size()
+    ws, nbytes = _workspace(workspace, mlp_rmsnorm_workspace_bytes(m, _dt(a), gate_up, down), a.device)
     _check(_lib.qdm_mlp_decode_rmsnorm(_dev(a, "a"), _dev(b, "b"), _dev(norm_w, "norm_w"), float(eps), m, _dt(a),
                                        ctypes.byref(gate_up.descriptor), ctypes.byref(down.descriptor),
-                                       _dev(workspace, "workspace"), nbytes,
+                                       ws, nbytes,
                                        None if s_out is None else _dev(s_out, "s_out"), _dev(out, "out"),
                                        _stream(stream)), "qdm_mlp_decode_rmsnorm")
     return out
@@ -446,6 +465,7 @@ def mlp_decode_rmsnorm(a, b, norm_w, eps: float, gate_up: Weight, down: Weight, 
 __all__ = [
     "Weight", "QdmError", "qdm_weight", "EXPORTS", "LIB_PATH",
     "status_string", "version", "packed_q_bytes", "scale_bias_floats", "mlp_workspace_bytes",
+    "gemv_gate_up_workspace_bytes", "gemv_down_workspace_bytes",
     "quantize_affine", "pack_rows", "quantize_pack_rows", "quantize_pack_gate_up", "pack_gate_up",
     "pack_dense_gate_up", "gemv_gate_up_swiglu", "gemv_down_residual", "gemv_linear", "mlp_decode", "add_rmsnorm",
     "mlp_rmsnorm_workspace_bytes", "mlp_decode_rmsnorm", "mx_scale_bytes", "quantize_mx", "quantize_mx_gate_up",

@@ -211,7 +211,7 @@ int run_bits(const qdm_weight& w, const void* x, const void* r, void* out, int n
 
 template <int XDT, int ODT, bool GU>
 int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, void* out,
-             int64_t o_row, int n_out, int k, int m, hipStream_t s) {
+             int64_t o_row, int n_out, int k, int m, float* part, hipStream_t s) {
     // one row: the streaming kernel while K fits 8 waves of 64 activations; otherwise (and for
     // several rows) the block-per-row-group kernel, rows in blocks of up to 4
     if (m == 1) {
@@ -245,7 +245,7 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
             return launch_gate_up_mma_stream(x, m, XDT, w, static_cast<float*>(out), s);
     } else {
         if (mma_stream_down_supported(w, m, ODT))
-            return launch_down_mma_stream(static_cast<const float*>(x), r, m, ODT, w, out, s);
+            return launch_down_mma_stream(static_cast<const float*>(x), r, m, ODT, w, out, part, s);
     }
     if (is_mx(w.bits) || is_sb16(w.bits)) return static_cast<int>(hipErrorInvalidValue);
     if (mma_rows_supported(w, m)) {
@@ -322,20 +322,20 @@ int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, f
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int ffn = gu.n, d = gu.k;
     switch (act) {
-        case DT_F32: return run_rows<DT_F32, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, s);
-        case DT_F16: return run_rows<DT_F16, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, s);
-        default: return run_rows<DT_BF16, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, s);
+        case DT_F32: return run_rows<DT_F32, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, nullptr, s);
+        case DT_F16: return run_rows<DT_F16, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, nullptr, s);
+        default: return run_rows<DT_BF16, DT_F32, true>(gu, x, d, nullptr, h, ffn, ffn, d, m, nullptr, s);
     }
 }
 
 int launch_down_residual(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
-                         void* stream) {
+                         float* part, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int d = dn.n, ffn = dn.k;
     switch (act) {
-        case DT_F32: return run_rows<DT_F32, DT_F32, false>(dn, h, ffn, r, out, d, d, ffn, m, s);
-        case DT_F16: return run_rows<DT_F32, DT_F16, false>(dn, h, ffn, r, out, d, d, ffn, m, s);
-        default: return run_rows<DT_F32, DT_BF16, false>(dn, h, ffn, r, out, d, d, ffn, m, s);
+        case DT_F32: return run_rows<DT_F32, DT_F32, false>(dn, h, ffn, r, out, d, d, ffn, m, part, s);
+        case DT_F16: return run_rows<DT_F32, DT_F16, false>(dn, h, ffn, r, out, d, d, ffn, m, part, s);
+        default: return run_rows<DT_F32, DT_BF16, false>(dn, h, ffn, r, out, d, d, ffn, m, part, s);
     }
 }
 

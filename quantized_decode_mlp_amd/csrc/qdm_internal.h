@@ -12,8 +12,10 @@ namespace qdm {
 // Each returns 0 on success or the hipError_t of the failed launch.
 int launch_gate_up_swiglu(const void* x, int m, int act, const qdm_weight& gu, float* h,
                           void* stream);
+// part: fp32 split-K partials, at least down_mma_stream_partials_bytes(dn, m)
+// when mma_stream_down_supported(dn, m, act) (unused otherwise).
 int launch_down_residual(const float* h, const void* r, int m, int act, const qdm_weight& dn,
-                         void* out, void* stream);
+                         void* out, float* part, void* stream);
 // True when one row of x (xb bytes per element) times w runs on the
 // weight-streaming kernel (the only kernel that takes MX weights).
 bool stream_supported(const qdm_weight& w, int xb);
@@ -32,25 +34,32 @@ int launch_gate_up_mma_stream(const void* x, int m, int act, const qdm_weight& g
 int launch_gate_up_mma_stream_norm(const void* a, const void* b, const void* w, float eps, int m, int act,
                                    const qdm_weight& gu, float* h, void* s_buf, void* stream);
 // 2..16 rows, 8/4-bit affine weights, 16-bit output: K split across blocks
-// with the partials in a device scratch the library allocates on first use
-// (qdm_mma_down.hip).
+// with the fp32 partials in part, a caller-owned buffer of at least
+// down_mma_stream_partials_bytes(dn, m) bytes (qdm_mma_down.hip).
 bool mma_stream_down_supported(const qdm_weight& w, int m, int act);
+size_t down_mma_stream_partials_bytes(const qdm_weight& w, int m);
 // r_copy: when not null, also receives r (the decode chain's s).
 int launch_down_mma_stream(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
-                           void* stream, void* r_copy = nullptr);
+                           float* part, void* stream, void* r_copy = nullptr);
 // One row, both projections on the streaming kernels: the decode chain with
 // add + RMSNorm folded into the MLP's two launches (qdm_chain.hip).
 bool chain_stream_supported(const qdm_weight& gu, const qdm_weight& dn, int act);
 int launch_mlp_chain_stream(const void* a, const void* b, const void* w, float eps, int act, const qdm_weight& gu,
                             const qdm_weight& dn, float* h, void* s_out, void* out, void* stream);
-// The device's fp32 partials buffer (at least bytes), shared by the split-K
-// kernels; grows outside graph capture only.  Null with err set on failure.
-float* partials_scratch(size_t bytes, void* stream, int& err);
 // More than 16 rows, 8/4-bit affine (either pair storage) or MX weights, 16-bit
 // activations: tiled dual GEMM, 64 rows x 64 outputs per block (qdm_prefill.hip).
+// A launch whose output tiles do not fill the chip splits K and writes fp32
+// partials to part, a caller-owned buffer of at least prefill_partials_bytes
+// (0: no split, part unused).
 bool prefill_supported(const qdm_weight& w, int m, int act);
-int launch_gate_up_prefill(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream);
-int launch_down_prefill(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, void* stream);
+size_t prefill_partials_bytes(const qdm_weight& w, int m, bool gate_up);
+int launch_gate_up_prefill(const void* x, int m, int act, const qdm_weight& gu, float* h, float* part, void* stream);
+int launch_down_prefill(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, float* part,
+                        void* stream);
+// qdm_mlp_decode after validation: h and the partials in `workspace`, laid
+// out for qdm_mlp_workspace_bytes(m, act, &gu, &dn) bytes (qdm_api.cpp).
+int mlp_decode_in(const void* x, const void* r, int32_t m, int act, const qdm_weight& gu, const qdm_weight& dn,
+                  void* workspace, void* out, void* stream);
 int launch_add_rmsnorm(const void* a, const void* b, const void* w, int rows, int n, float eps,
                        int dtype, void* s_out, void* n_out, void* stream);
 

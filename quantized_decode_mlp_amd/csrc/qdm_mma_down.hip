@@ -13,7 +13,7 @@
 // fold chunk, then streams 16-row weight tiles of that slice through
 // v_mfma_f32_16x16x32_bf16 (two MMAs per k-step, hi and lo) with the codes as
 // exact operands and each chunk's partial folded as in the gate/up kernel;
-// the partial tile goes to part[s][m][n] (a scratch buffer of the device).  Kernel 2 adds the NS partials in
+// the partial tile goes to part[s][m][n] (in the caller's workspace).  Kernel 2 adds the NS partials in
 // slice order and the residual and rounds to the output type.  Work split,
 // lane layout and scale/bias handling match the gate/up kernel: S waves take
 // contiguous quarters of a tile's k-range in the slice, P tiles per block,
@@ -22,9 +22,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "qdm_device.h"
 #include "qdm_internal.h"
@@ -319,50 +316,11 @@ bool pick_down_split(int m, int n, int k, int cus, DownSplit& out) {
 
 }  // namespace
 
-// Partials scratch, one per device, grown on demand.  Growth happens only
-// outside graph capture and after the device has drained, since work on any
-// stream may still use the old buffer.
-float* partials_scratch(size_t bytes, void* stream, int& err) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    static std::mutex mu;
-    static std::map<int, std::pair<void*, size_t>> bufs;
-    err = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        err = static_cast<int>(hipErrorInvalidDevice);
-        return nullptr;
-    }
-    std::lock_guard<std::mutex> lk(mu);
-    auto& b = bufs[dev];
-    if (b.second >= bytes) return static_cast<float*>(b.first);
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-        err = static_cast<int>(hipErrorStreamCaptureUnsupported);
-        return nullptr;
-    }
-    if (b.first) {
-        const hipError_t e = hipDeviceSynchronize();
-        if (e != hipSuccess) {
-            err = static_cast<int>(e);
-            return nullptr;
-        }
-        (void)hipFree(b.first);   // the device has drained; a failure here leaves nothing to undo
-        b = {nullptr, 0};
-    }
-    void* p = nullptr;
-    const hipError_t e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) {
-        err = static_cast<int>(e);
-        return nullptr;
-    }
-    b = {p, bytes};
-    return static_cast<float*>(p);
-}
-
 namespace {
 
 template <int BITS, int G, int ODT>
-int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* r_copy) {
+int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, float* part,
+             void* r_copy) {
     constexpr int NT = 64 * kDS * kDP;
     constexpr int U = kDU;
     int dev = 0, cus = 0;
@@ -371,9 +329,7 @@ int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int 
     DownSplit sp;
     if (!pick_down_split<BITS, G>(m, w.n, w.k, cus, sp)) return static_cast<int>(hipErrorInvalidValue);
     const int ns = w.k / sp.kr;
-    int err = 0;
-    float* part = partials_scratch(static_cast<size_t>(ns) * m * w.n * sizeof(float), s, err);
-    if (!part) return err;
+    if (!part) return static_cast<int>(hipErrorInvalidValue);
     auto kern = qmm_down_part_kernel<BITS, G, kDS, kDP, U, pair_regs<G>()>;
     const size_t lds = down_lds_bytes<BITS, G>(m, sp.kr);
     if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -392,30 +348,44 @@ int run_down(const qdm_weight& w, const float* h, const void* r, void* out, int 
 }
 
 template <int BITS, int ODT>
-int run_down_g(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* rc) {
+int run_down_g(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, float* part,
+               void* rc) {
     switch (w.group) {
-        case 32: return run_down<BITS, 32, ODT>(w, h, r, out, m, s, rc);
-        case 64: return run_down<BITS, 64, ODT>(w, h, r, out, m, s, rc);
-        default: return run_down<BITS, 128, ODT>(w, h, r, out, m, s, rc);
+        case 32: return run_down<BITS, 32, ODT>(w, h, r, out, m, s, part, rc);
+        case 64: return run_down<BITS, 64, ODT>(w, h, r, out, m, s, part, rc);
+        default: return run_down<BITS, 128, ODT>(w, h, r, out, m, s, part, rc);
     }
 }
 
 template <int ODT>
-int run_down_b(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, void* rc) {
+int run_down_b(const qdm_weight& w, const float* h, const void* r, void* out, int m, hipStream_t s, float* part,
+               void* rc) {
     switch (w.bits) {
-        case 8: return run_down_g<8, ODT>(w, h, r, out, m, s, rc);
-        case QDM_U8_SB16: return run_down_g<QDM_U8_SB16, ODT>(w, h, r, out, m, s, rc);
-        case QDM_U4_SB16: return run_down_g<QDM_U4_SB16, ODT>(w, h, r, out, m, s, rc);
-        case QDM_MXFP8: return run_down<QDM_MXFP8, 32, ODT>(w, h, r, out, m, s, rc);
-        case QDM_MXFP4: return run_down<QDM_MXFP4, 32, ODT>(w, h, r, out, m, s, rc);
-        default: return run_down_g<4, ODT>(w, h, r, out, m, s, rc);
+        case 8: return run_down_g<8, ODT>(w, h, r, out, m, s, part, rc);
+        case QDM_U8_SB16: return run_down_g<QDM_U8_SB16, ODT>(w, h, r, out, m, s, part, rc);
+        case QDM_U4_SB16: return run_down_g<QDM_U4_SB16, ODT>(w, h, r, out, m, s, part, rc);
+        case QDM_MXFP8: return run_down<QDM_MXFP8, 32, ODT>(w, h, r, out, m, s, part, rc);
+        case QDM_MXFP4: return run_down<QDM_MXFP4, 32, ODT>(w, h, r, out, m, s, part, rc);
+        default: return run_down_g<4, ODT>(w, h, r, out, m, s, part, rc);
     }
 }
 
+// Slices of the split (0 when no split fits); the slice count does not depend
+// on the device, only the tile groups per slice do.
 template <int BITS, int G>
-bool split_exists(int m, int n, int k) {
+int split_slices(int m, int n, int k) {
     DownSplit sp;
-    return pick_down_split<BITS, G>(m, n, k, 1, sp);
+    return pick_down_split<BITS, G>(m, n, k, 1, sp) ? k / sp.kr : 0;
+}
+
+int down_slices(const qdm_weight& w, int m) {
+    if (w.bits == QDM_MXFP8) return w.group == 32 ? split_slices<QDM_MXFP8, 32>(m, w.n, w.k) : 0;
+    if (w.bits == QDM_MXFP4) return w.group == 32 ? split_slices<QDM_MXFP4, 32>(m, w.n, w.k) : 0;
+    if (code_width(w.bits) == 4)
+        return w.group == 32 ? split_slices<4, 32>(m, w.n, w.k)
+             : w.group == 64 ? split_slices<4, 64>(m, w.n, w.k) : split_slices<4, 128>(m, w.n, w.k);
+    return w.group == 32 ? split_slices<8, 32>(m, w.n, w.k)
+         : w.group == 64 ? split_slices<8, 64>(m, w.n, w.k) : split_slices<8, 128>(m, w.n, w.k);
 }
 
 }  // namespace
@@ -426,20 +396,19 @@ bool mma_stream_down_supported(const qdm_weight& w, int m, int act) {
     if (w.group != 32 && w.group != 64 && w.group != 128) return false;
     if (act != DT_BF16 && act != DT_F16) return false;   // h enters at ~16 bits: 16-bit outputs only
     if (w.n % kRows != 0) return false;
-    if (w.bits == QDM_MXFP8) return w.group == 32 && split_exists<QDM_MXFP8, 32>(m, w.n, w.k);
-    if (w.bits == QDM_MXFP4) return w.group == 32 && split_exists<QDM_MXFP4, 32>(m, w.n, w.k);
-    if (code_width(w.bits) == 4)
-        return w.group == 32 ? split_exists<4, 32>(m, w.n, w.k)
-             : w.group == 64 ? split_exists<4, 64>(m, w.n, w.k) : split_exists<4, 128>(m, w.n, w.k);
-    return w.group == 32 ? split_exists<8, 32>(m, w.n, w.k)
-         : w.group == 64 ? split_exists<8, 64>(m, w.n, w.k) : split_exists<8, 128>(m, w.n, w.k);
+    return down_slices(w, m) > 0;
+}
+
+size_t down_mma_stream_partials_bytes(const qdm_weight& w, int m) {
+    return static_cast<size_t>(down_slices(w, m)) * static_cast<size_t>(m) * static_cast<size_t>(w.n) *
+           sizeof(float);
 }
 
 int launch_down_mma_stream(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out,
-                           void* stream, void* r_copy) {
+                           float* part, void* stream, void* r_copy) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return act == DT_F16 ? run_down_b<DT_F16>(dn, h, r, out, m, s, r_copy)
-                         : run_down_b<DT_BF16>(dn, h, r, out, m, s, r_copy);
+    return act == DT_F16 ? run_down_b<DT_F16>(dn, h, r, out, m, s, part, r_copy)
+                         : run_down_b<DT_BF16>(dn, h, r, out, m, s, part, r_copy);
 }
 
 }  // namespace qdm

@@ -33,13 +33,15 @@
 //
 // Split K.  When the output tiles alone do not fill the chip, the k-blocks
 // are split over S slices; a slice's tile goes to fp32 partials
-// part[s][m][n'] in the library's device scratch and a second kernel adds the
+// part[s][m][n'] in the caller's workspace and a second kernel adds the
 // slices in order (so results do not depend on timing) and applies SwiGLU
 // (gate/up) or the residual and the output rounding (down).
 //
 // Gate/up takes the activations in their own 16-bit type; down takes the fp32
 // hidden rows as a bf16 high part and the bf16 remainder (two MMAs per
 // fragment and step, about 16 significant bits).
+#include <algorithm>
+
 #include "qdm_internal.h"
 #include "qdm_launch.h"
 #include "qdm_mma_common.h"
@@ -391,38 +393,50 @@ constexpr int kNoGateUp = 1;   // output fragments per wave (gate/up)
 constexpr int kNoDown = 2;     // output fragments per wave (down)
 
 // Slices: doubled until there are two blocks per compute unit, each slice
-// keeping at least two k-blocks.
+// keeping at least two k-blocks.  The CU count is capped at the full gfx950
+// chip's 256, so the partials' size for the full chip (what the workspace
+// queries report) bounds every device this runs on.
+constexpr int kMaxCus = 256;
+
 int pick_slices(int tiles, int nkb, int cus) {
+    cus = std::min(cus, kMaxCus);
     int s = 1;
     while (tiles * s < 2 * cus && 4 * s <= nkb && s < 16) s *= 2;
     return s;
 }
 
-template <int BITS, int G, int XDT, bool GU, int ODT>
-int run_prefill(const qdm_weight& w, const void* x, const void* r, void* out, int m, hipStream_t s) {
+// Output tiles of a projection and its k-blocks, as the launcher lays them out.
+template <int BITS, int G, bool GU>
+void prefill_grid(const qdm_weight& w, int m, int& nb, int& mb, int& nkb) {
     constexpr int NO = GU ? kNoGateUp : kNoDown;
-    using L = TileLayout<BITS, G>;
+    const int bn = 16 * NO * kPW;
+    nb = (w.n + bn - 1) / bn;
+    mb = (m + kPBM - 1) / kPBM;
+    nkb = w.k / TileLayout<BITS, G>::KBK;
+}
+
+template <int BITS, int G, int XDT, bool GU, int ODT>
+int run_prefill(const qdm_weight& w, const void* x, const void* r, void* out, int m, float* part, hipStream_t s) {
+    constexpr int NO = GU ? kNoGateUp : kNoDown;
     auto kern = qmm_prefill_kernel<BITS, G, XDT, GU, ODT, NO>;
     const float* sbp = mx_bits(BITS) ? reinterpret_cast<const float*>(w.block_scales) : w.scale_bias;
     if (!sbp) return static_cast<int>(hipErrorInvalidValue);
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return static_cast<int>(hipErrorInvalidDevice);
-    const int bn = 16 * NO * kPW;
-    const int nb = (w.n + bn - 1) / bn, mb = (m + kPBM - 1) / kPBM;
-    const int S = pick_slices(nb * mb, w.k / L::KBK, cus);
+    int nb = 0, mb = 0, nkb = 0;
+    prefill_grid<BITS, G, GU>(w, m, nb, mb, nkb);
+    const int S = pick_slices(nb * mb, nkb, cus);
     constexpr size_t lds = prefill_lds_bytes<BITS, G, GU>();
     if (lds > 65536 && hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
         return static_cast<int>(hipErrorInvalidValue);
-    float* part = nullptr;
-    if (S > 1) {
-        int err = 0;
-        part = partials_scratch(static_cast<size_t>(S) * m * w.n * (GU ? 2 : 1) * sizeof(float), s, err);
-        if (!part) return err;
-    }
+    if (S > 1 && !part) return static_cast<int>(hipErrorInvalidValue);
+    // the kernel writes partials exactly when it is given a buffer for them:
+    // an unsplit launch gets none, whatever the caller's workspace holds
+    float* kpart = S > 1 ? part : nullptr;
     hipError_t e = launch(kern, dim3(nb * S, mb), dim3(kPT), lds, s, static_cast<const uint8_t*>(w.q), sbp, x, r,
-                          out, part, w.n, w.k, m, S);
+                          out, kpart, w.n, w.k, m, S);
     if (e != hipSuccess || S == 1) return static_cast<int>(e);
     const int64_t outs = static_cast<int64_t>(m) * w.n;
     e = launch(qmm_prefill_reduce_kernel<GU, ODT>, dim3(static_cast<unsigned>((outs + 255) / 256)), dim3(256), 0, s,
@@ -431,23 +445,55 @@ int run_prefill(const qdm_weight& w, const void* x, const void* r, void* out, in
 }
 
 template <int XDT, bool GU, int ODT, int G>
-int run_prefill_b(const qdm_weight& w, const void* x, const void* r, void* out, int m, hipStream_t s) {
+int run_prefill_b(const qdm_weight& w, const void* x, const void* r, void* out, int m, float* part, hipStream_t s) {
     switch (w.bits) {
-        case 8: return run_prefill<8, G, XDT, GU, ODT>(w, x, r, out, m, s);
-        case 4: return run_prefill<4, G, XDT, GU, ODT>(w, x, r, out, m, s);
-        case QDM_U8_SB16: return run_prefill<QDM_U8_SB16, G, XDT, GU, ODT>(w, x, r, out, m, s);
-        default: return run_prefill<QDM_U4_SB16, G, XDT, GU, ODT>(w, x, r, out, m, s);
+        case 8: return run_prefill<8, G, XDT, GU, ODT>(w, x, r, out, m, part, s);
+        case 4: return run_prefill<4, G, XDT, GU, ODT>(w, x, r, out, m, part, s);
+        case QDM_U8_SB16: return run_prefill<QDM_U8_SB16, G, XDT, GU, ODT>(w, x, r, out, m, part, s);
+        default: return run_prefill<QDM_U4_SB16, G, XDT, GU, ODT>(w, x, r, out, m, part, s);
     }
 }
 
 template <int XDT, bool GU, int ODT>
-int run_prefill_g(const qdm_weight& w, const void* x, const void* r, void* out, int m, hipStream_t s) {
-    if (w.bits == QDM_MXFP8) return run_prefill<QDM_MXFP8, 32, XDT, GU, ODT>(w, x, r, out, m, s);
-    if (w.bits == QDM_MXFP4) return run_prefill<QDM_MXFP4, 32, XDT, GU, ODT>(w, x, r, out, m, s);
+int run_prefill_g(const qdm_weight& w, const void* x, const void* r, void* out, int m, float* part, hipStream_t s) {
+    if (w.bits == QDM_MXFP8) return run_prefill<QDM_MXFP8, 32, XDT, GU, ODT>(w, x, r, out, m, part, s);
+    if (w.bits == QDM_MXFP4) return run_prefill<QDM_MXFP4, 32, XDT, GU, ODT>(w, x, r, out, m, part, s);
     switch (w.group) {
-        case 32: return run_prefill_b<XDT, GU, ODT, 32>(w, x, r, out, m, s);
-        case 64: return run_prefill_b<XDT, GU, ODT, 64>(w, x, r, out, m, s);
-        default: return run_prefill_b<XDT, GU, ODT, 128>(w, x, r, out, m, s);
+        case 32: return run_prefill_b<XDT, GU, ODT, 32>(w, x, r, out, m, part, s);
+        case 64: return run_prefill_b<XDT, GU, ODT, 64>(w, x, r, out, m, part, s);
+        default: return run_prefill_b<XDT, GU, ODT, 128>(w, x, r, out, m, part, s);
+    }
+}
+
+// Bytes of fp32 partials a split launch writes with the full chip's CU count
+// (0 when the projection runs unsplit).
+template <int BITS, int G, bool GU>
+size_t partials_for(const qdm_weight& w, int m) {
+    int nb = 0, mb = 0, nkb = 0;
+    prefill_grid<BITS, G, GU>(w, m, nb, mb, nkb);
+    const int S = pick_slices(nb * mb, nkb, kMaxCus);
+    if (S == 1) return 0;
+    return static_cast<size_t>(S) * static_cast<size_t>(m) * static_cast<size_t>(w.n) * (GU ? 2 : 1) * sizeof(float);
+}
+
+template <bool GU, int G>
+size_t partials_b(const qdm_weight& w, int m) {
+    switch (w.bits) {
+        case 8: return partials_for<8, G, GU>(w, m);
+        case 4: return partials_for<4, G, GU>(w, m);
+        case QDM_U8_SB16: return partials_for<QDM_U8_SB16, G, GU>(w, m);
+        default: return partials_for<QDM_U4_SB16, G, GU>(w, m);
+    }
+}
+
+template <bool GU>
+size_t partials_g(const qdm_weight& w, int m) {
+    if (w.bits == QDM_MXFP8) return partials_for<QDM_MXFP8, 32, GU>(w, m);
+    if (w.bits == QDM_MXFP4) return partials_for<QDM_MXFP4, 32, GU>(w, m);
+    switch (w.group) {
+        case 32: return partials_b<GU, 32>(w, m);
+        case 64: return partials_b<GU, 64>(w, m);
+        default: return partials_b<GU, 128>(w, m);
     }
 }
 
@@ -464,16 +510,21 @@ bool prefill_supported(const qdm_weight& w, int m, int act) {
     return w.n % 16 == 0 && w.k % kbk == 0;
 }
 
-int launch_gate_up_prefill(const void* x, int m, int act, const qdm_weight& gu, float* h, void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return act == DT_F16 ? run_prefill_g<DT_F16, true, DT_F32>(gu, x, nullptr, h, m, s)
-                         : run_prefill_g<DT_BF16, true, DT_F32>(gu, x, nullptr, h, m, s);
+size_t prefill_partials_bytes(const qdm_weight& w, int m, bool gate_up) {
+    return gate_up ? partials_g<true>(w, m) : partials_g<false>(w, m);
 }
 
-int launch_down_prefill(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, void* stream) {
+int launch_gate_up_prefill(const void* x, int m, int act, const qdm_weight& gu, float* h, float* part, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return act == DT_F16 ? run_prefill_g<DT_F32, false, DT_F16>(dn, h, r, out, m, s)
-                         : run_prefill_g<DT_F32, false, DT_BF16>(dn, h, r, out, m, s);
+    return act == DT_F16 ? run_prefill_g<DT_F16, true, DT_F32>(gu, x, nullptr, h, m, part, s)
+                         : run_prefill_g<DT_BF16, true, DT_F32>(gu, x, nullptr, h, m, part, s);
+}
+
+int launch_down_prefill(const float* h, const void* r, int m, int act, const qdm_weight& dn, void* out, float* part,
+                        void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return act == DT_F16 ? run_prefill_g<DT_F32, false, DT_F16>(dn, h, r, out, m, part, s)
+                         : run_prefill_g<DT_F32, false, DT_BF16>(dn, h, r, out, m, part, s);
 }
 
 }  // namespace qdm

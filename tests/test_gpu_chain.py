@@ -127,7 +127,7 @@ def test_chain_graph_replay():
     _, (gu, dn) = workload_case(4)
     a, b, w = W.chain_inputs(wl, 1)
     ad, bd, wd = to_device(a), to_device(b), to_device(w)
-    ws = torch.empty(qdm.mlp_rmsnorm_workspace_bytes(1, wl.d, wl.ffn, qdm.QDM_BF16), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(qdm.mlp_rmsnorm_workspace_bytes(1, qdm.QDM_BF16, gu, dn), dtype=torch.uint8, device="cuda")
     out, s = torch.empty_like(ad), torch.empty_like(ad)
     eager = qdm.mlp_decode_rmsnorm(ad, bd, wd, EPS, gu, dn, workspace=ws, s_out=s).clone()
     s_eager = s.clone()
@@ -174,7 +174,7 @@ def test_chain_rows_in_place_and_graph():
     qdm.mlp_decode_rmsnorm(a2, b2, w, EPS, gu, dn, s_out=a2, out=b2)
     torch.cuda.synchronize()
     assert torch.equal(a2, s_u) and torch.equal(b2, y_u)
-    ws = torch.empty(qdm.mlp_rmsnorm_workspace_bytes(m, d, ffn, qdm.QDM_BF16), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(qdm.mlp_rmsnorm_workspace_bytes(m, qdm.QDM_BF16, gu, dn), dtype=torch.uint8, device="cuda")
     out, s = torch.empty_like(a), torch.empty_like(a)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):

@@ -200,16 +200,16 @@ def test_rows_are_independent(bits, group):
 @pytest.mark.parametrize("m", [4, 16])
 @pytest.mark.parametrize("bits,group", [(4, 64), (8, 128)])
 def test_rows_graph_replay(m, bits, group):
-    """A few-row MLP captured into a HIP graph after one eager call (which
-    sizes the down projection's scratch) replays bitwise equal to the eager
-    result, with other work between replays, and meets the oracle bar."""
+    """A few-row MLP captured into a HIP graph after one eager call replays
+    bitwise equal to the eager result, with other work between replays, and
+    meets the oracle bar."""
     qdm = _qdm()
     d, ffn = 1024, 1536
     ow, (gu, dn) = generic_case((91, bits, m), d, ffn, bits, group)
     x = W.generic_act((m, 8), (m, d), "bf16")
     r = W.generic_act((m, 9), (m, d), "bf16")
     xd, rd = to_device(x), to_device(r)
-    ws = torch.empty(qdm.mlp_workspace_bytes(m, ffn), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(qdm.mlp_workspace_bytes(m, qdm.QDM_BF16, gu, dn), dtype=torch.uint8, device="cuda")
     y_eager = qdm.mlp_decode(xd, rd, gu, dn, workspace=ws).clone()
     torch.cuda.synchronize()
     out = torch.empty_like(rd)
