@@ -75,7 +75,8 @@ typedef enum qdm_status {
     QDM_ERR_UNSUPPORTED = -2,   /* valid but not provided: bits/group/dtype/row-count combination */
     QDM_ERR_ALIGNMENT = -3,     /* a pointer is not aligned as the entry point requires */
     QDM_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than its *_workspace_bytes() query */
-    QDM_ERR_HIP = -5            /* the HIP runtime refused a launch */
+    QDM_ERR_HIP = -5,           /* the HIP runtime refused a launch */
+    QDM_ERR_TOO_LARGE = -6      /* qdm_mlp_decode_noalloc: the call needs more than its fixed scratch */
 } qdm_status;
 
 typedef enum qdm_dtype { QDM_F32 = 0, QDM_F16 = 1, QDM_BF16 = 2 } qdm_dtype;
@@ -299,6 +300,25 @@ int qdm_gemv_linear(const void* x, int32_t m, qdm_dtype act, const qdm_weight* w
 int qdm_mlp_decode(const void* x, const void* r, int32_t m, qdm_dtype act,
                    const qdm_weight* gate_up, const qdm_weight* down,
                    void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* qdm_mlp_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, with the workspace (h and the split-K
+ * partials) in a fixed array of QDM_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends, instead of a caller's
+ * buffer.  Arguments as for qdm_mlp_decode without the workspace.
+ * QDM_ERR_TOO_LARGE when qdm_mlp_workspace_bytes(m, act, gate_up, down)
+ * exceeds the array (16 MiB: h and partials of up to 16 rows at Llama-3-8B
+ * and Qwen3-8B shapes; more rows need the ordinary entry point); nothing is
+ * launched then.  The array keeps the last call's contents; the kernels write
+ * every byte they read, so nothing is cleared between calls.  All calls on one
+ * GPU share its array: calls that can overlap in time on that GPU (different
+ * streams, or threads without ordering) race and must be ordered by the
+ * caller.  Allocates nothing: the array's device address is looked up once
+ * per device, on the first call made with that device current. */
+#define QDM_NOALLOC_SCRATCH_BYTES (16u << 20)
+int qdm_mlp_decode_noalloc(const void* x, const void* r, int32_t m, qdm_dtype act,
+                           const qdm_weight* gate_up, const qdm_weight* down, void* out, void* stream);
 
 /* Residual add + RMSNorm with both outputs, per row ("Compute-Graph Fusion",
  * the opening GraphBuilder example: the add feeds RMSNorm and the sum stays a

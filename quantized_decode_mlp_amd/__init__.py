@@ -24,6 +24,8 @@ QDM_ERR_UNSUPPORTED = -2
 QDM_ERR_ALIGNMENT = -3
 QDM_ERR_WORKSPACE = -4
 QDM_ERR_HIP = -5
+QDM_ERR_TOO_LARGE = -6
+NOALLOC_SCRATCH_BYTES = 16 << 20   # QDM_NOALLOC_SCRATCH_BYTES
 
 QDM_F32, QDM_F16, QDM_BF16 = 0, 1, 2
 QDM_MXFP4, QDM_MXFP8 = 0x104, 0x108       # qdm_weight.bits of the MX block-scaled formats
@@ -36,6 +38,7 @@ EXPORTS = (
     "qdm_quantize_affine", "qdm_pack_rows", "qdm_quantize_pack_rows",
     "qdm_quantize_pack_gate_up", "qdm_pack_gate_up", "qdm_pack_dense_gate_up",
     "qdm_gemv_gate_up_swiglu", "qdm_gemv_down_residual", "qdm_gemv_linear", "qdm_mlp_decode",
+    "qdm_mlp_decode_noalloc",
     "qdm_add_rmsnorm", "qdm_mlp_rmsnorm_workspace_bytes", "qdm_mlp_decode_rmsnorm",
     "qdm_mx_scale_bytes", "qdm_quantize_mx", "qdm_quantize_mx_gate_up",
     "qdm_quantize_pack_rows_sb16", "qdm_quantize_pack_gate_up_sb16",
@@ -83,6 +86,7 @@ def _load():
         "qdm_gemv_linear": (ctypes.c_int, [vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight), vp, vp, vp]),
         "qdm_mlp_decode": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
                                           ctypes.POINTER(qdm_weight), vp, sz, vp, vp]),
+        "qdm_mlp_decode_noalloc": (ctypes.c_int, [vp, vp, i32, ctypes.c_int, pw, pw, vp, vp]),
         "qdm_add_rmsnorm": (ctypes.c_int, [vp, vp, vp, i32, i32, f32, ctypes.c_int, vp, vp, vp]),
         "qdm_mlp_rmsnorm_workspace_bytes": (sz, [i32, ctypes.c_int, pw, pw]),
         "qdm_mlp_decode_rmsnorm": (ctypes.c_int, [vp, vp, vp, f32, i32, ctypes.c_int, ctypes.POINTER(qdm_weight),
@@ -426,6 +430,22 @@ def mlp_decode(x, r, gate_up: Weight, down: Weight, workspace=None, out=None, st
     return out
 
 
+def mlp_decode_noalloc(x, r, gate_up: Weight, down: Weight, out=None, stream=None):
+    """mlp_decode with the workspace in the library's fixed per-device array
+    (NOALLOC_SCRATCH_BYTES): no allocation anywhere when ``out`` is given."""
+    m = x.shape[0] if x.dim() == 2 else 1
+    if x.dtype != r.dtype:
+        raise TypeError("x and r must share a dtype")
+    if out is None:
+        out = _torch().empty_like(r)
+    if out.dtype != r.dtype:
+        raise TypeError("out must have the dtype of r")
+    _check(_lib.qdm_mlp_decode_noalloc(_dev(x, "x"), _dev(r, "r"), m, _dt(x), ctypes.byref(gate_up.descriptor),
+                                       ctypes.byref(down.descriptor), _dev(out, "out"), _stream(stream)),
+           "qdm_mlp_decode_noalloc")
+    return out
+
+
 def add_rmsnorm(a, b, w, eps: float, s_out=None, n_out=None, stream=None):
     """s = a + b, n = rmsnorm(s) * w; returns (s, n) in the dtype of a."""
     torch = _torch()
@@ -468,6 +488,7 @@ __all__ = [
     "gemv_gate_up_workspace_bytes", "gemv_down_workspace_bytes",
     "quantize_affine", "pack_rows", "quantize_pack_rows", "quantize_pack_gate_up", "pack_gate_up",
     "pack_dense_gate_up", "gemv_gate_up_swiglu", "gemv_down_residual", "gemv_linear", "mlp_decode", "add_rmsnorm",
+    "mlp_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "mlp_rmsnorm_workspace_bytes", "mlp_decode_rmsnorm", "mx_scale_bytes", "quantize_mx", "quantize_mx_gate_up",
     "quantize_pack_rows_sb16", "quantize_pack_gate_up_sb16",
 ]

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libqdm.so")
 ARCH = "gfx950"
 HOST_SOURCES = ["qdm_pack.cpp", "qdm_api.cpp"]
 HIP_SOURCES = ["qdm_gemv.hip", "qdm_mfma.hip", "qdm_mma_stream.hip", "qdm_mma_down.hip", "qdm_rmsnorm.hip",
-               "qdm_chain.hip", "qdm_prefill.hip"]
+               "qdm_chain.hip", "qdm_prefill.hip", "qdm_noalloc.hip"]
 
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-pthread",
               "-Wall", "-Wextra", "-Wno-unused-parameter"]

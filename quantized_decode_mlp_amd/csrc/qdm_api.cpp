@@ -335,6 +335,7 @@ const char* qdm_status_string(int status) {
         case QDM_ERR_ALIGNMENT: return "misaligned pointer";
         case QDM_ERR_WORKSPACE: return "workspace missing or too small";
         case QDM_ERR_HIP: return "HIP launch failed";
+        case QDM_ERR_TOO_LARGE: return "call exceeds the fixed scratch of the allocation-free entry point";
         default: return "unknown status";
     }
 }
