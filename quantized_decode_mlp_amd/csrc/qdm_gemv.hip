@@ -217,6 +217,7 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
     if (m == 1) {
         StreamSplit sp;
         if (stream_split(w.bits, k, x_bytes<XDT>(), sp)) {
+            sp.nr = stream_rows_per_group(sp, GU);
             switch (w.bits) {
                 case 8: return run_stream<8, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
                 case 4: return run_stream<4, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
@@ -275,6 +276,7 @@ int run_linear(const qdm_weight& w, const void* x, int m, const void* bias, void
     const int n = w.n, k = w.k;
     StreamSplit sp;
     if (m == 1 && stream_split(w.bits, k, x_bytes<XDT>(), sp)) {
+        sp.nr = stream_rows_per_group(sp, false);
         switch (w.bits) {
             case 8: return run_stream<8, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});
             case 4: return run_stream<4, XDT, XDT, false, kEpiLinear>(w, x, bias, out, n, k, sp, s, ChainArgs{});

@@ -100,15 +100,20 @@ constexpr int x_bytes() { return XDT == DT_F32 ? 4 : 2; }
 
 // Stream (block b, p) takes groups b*P + p + i*G*P for rounds i = 0, 1, ...
 // (G = gridDim); every wave walks the same number of rounds, so the block's
-// barriers line up even when a stream has run out of groups.
-template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P, int EPI>
-__global__ void __launch_bounds__(64 * S * P)
+// barriers line up even when a stream has run out of groups.  A group is NR
+// consecutive outputs: gate/up pairs (GU), or rows of the other projections.
+// With NR = 2 a wave keeps two outputs' loads in flight per round against the
+// one activation slice it holds: twice the bytes in flight for the same
+// activation registers, for splits whose waves hold a single K-tile.
+template <int BITS, int XDT, int ODT, bool GU, int S, int TW, int P, int EPI, int NR>
+__global__ void __launch_bounds__(64 * S * P) __attribute__((amdgpu_waves_per_eu(NR == 2 ? S * P / 2 : 1)))
 qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                     const void* __restrict__ xin, const void* __restrict__ resid, void* __restrict__ out,
                     int n_out, int k, int gshift, ChainArgs ch) {
     constexpr int E = StreamShape<BITS>::E;
     constexpr int EPD = E / 4;
-    constexpr int NV = GU ? 2 : 1;
+    constexpr int NV = GU ? 2 * NR : NR;   // packed rows loaded per group
+    static_assert(NR == 1 || NR == 2, "one or two outputs per group");
     constexpr bool MX = is_mx(BITS);
     constexpr int CB = code_bits(BITS);
     constexpr bool SB16 = is_sb16(BITS);                 // affine with bf16 (scale, bias) pairs
@@ -133,7 +138,8 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     const int nbk = MX ? (k >> 5) : 0;                            // MX: scale bytes per row
     const int GP = static_cast<int>(gridDim.x) * P;
     const int g0 = static_cast<int>(blockIdx.x) * P + p;
-    const int rounds = (n_out - static_cast<int>(blockIdx.x) * P + GP - 1) / GP;   // same for every wave
+    const int n_grp = (n_out + NR - 1) / NR;   // groups of NR outputs (pairs for gate/up)
+    const int rounds = (n_grp - static_cast<int>(blockIdx.x) * P + GP - 1) / GP;   // same for every wave
     if (rounds <= 0) return;   // uniform per block, before any barrier
 
     // first pieces of the activation row (issued before the weights: the
@@ -176,12 +182,14 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     u32x4 wbuf[NV][TW];
     ChunkScale pbuf[NV][TW];
 
-    // loads of group grp (rows clamped; a stream past its last group reloads row n_out - 1)
+    // loads of group grp (rows clamped; a stream past its last group reloads the last row)
     auto issue = [&](u32x4 (&wq)[NV][TW], ChunkScale (&pp)[NV][TW], int grp) {
-        const uint32_t row = static_cast<uint32_t>(min(grp, n_out - 1));
+        const uint32_t row = static_cast<uint32_t>(min(grp, n_grp - 1));
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const uint32_t prow = GU ? 2u * row + v : row;
+            const uint32_t prow =
+                GU ? 2u * static_cast<uint32_t>(min(NR * static_cast<int>(row) + v / 2, n_out - 1)) + (v & 1)
+                   : static_cast<uint32_t>(min(NR * static_cast<int>(row) + v, n_out - 1));
             const uint8_t* qrow = q + static_cast<size_t>(prow) * rb;
             const uint8_t* srow =
                 reinterpret_cast<const uint8_t*>(sb) + static_cast<size_t>(prow) * (MX ? nbk : ng * (SB16 ? 4 : 8));
@@ -199,7 +207,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     };
 
     // the first round goes in flight before the activations are set up
-    if (g0 < n_out) issue(wbuf, pbuf, g0);
+    if (g0 < n_grp) issue(wbuf, pbuf, g0);
 
     if constexpr (NORM) {
         // The decode chain's RMSNorm, recomputed by every block from a, b and w
@@ -367,20 +375,31 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                 xp[j][i] = (__float_as_uint(xv[j][2 * i]) >> 16) | (__float_as_uint(xv[j][2 * i + 1]) & 0xffff0000u);
     }
 
-    auto epilogue = [&](int grp, const float (&t)[NV]) {
-        if constexpr (GU) {
-            const float gs = t[0];
-            static_cast<float*>(out)[grp] = gs / (1.0f + expf(-gs)) * t[NV - 1];
-        } else if constexpr (EPI == kEpiChain) {
+    // output row o of a single-row projection gets the dot product t
+    auto store_row = [&](int o, float t) {
+        if constexpr (EPI == kEpiChain) {
             // the residual is the chain's sum s = a + b, rounded once as stored
-            const float sv = round_trip<ODT>(load_elem<ODT>(ch.a, grp) + load_elem<ODT>(ch.b, grp));
-            if (ch.s_out) store_elem<ODT>(ch.s_out, grp, sv);
-            store_elem<ODT>(out, grp, sv + t[0]);
+            const float sv = round_trip<ODT>(load_elem<ODT>(ch.a, o) + load_elem<ODT>(ch.b, o));
+            if (ch.s_out) store_elem<ODT>(ch.s_out, o, sv);
+            store_elem<ODT>(out, o, sv + t);
         } else if constexpr (EPI == kEpiLinear) {
             // a projection: the optional bias takes the residual's place
-            store_elem<ODT>(out, grp, resid ? load_elem<ODT>(resid, grp) + t[0] : t[0]);
+            store_elem<ODT>(out, o, resid ? load_elem<ODT>(resid, o) + t : t);
         } else {
-            store_elem<ODT>(out, grp, load_elem<ODT>(resid, grp) + t[0]);
+            store_elem<ODT>(out, o, load_elem<ODT>(resid, o) + t);
+        }
+    };
+    auto epilogue = [&](int grp, const float (&t)[NV]) {
+        if constexpr (GU) {
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                const float gs = t[2 * j];
+                if (NR * grp + j < n_out) static_cast<float*>(out)[NR * grp + j] = gs / (1.0f + expf(-gs)) * t[2 * j + 1];
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                if (NR * grp + v < n_out) store_row(NR * grp + v, t[v]);
         }
     };
 
@@ -391,7 +410,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         if (t < cnt * P) {
             const int slot = t / P, sp = t % P;
             const int grp = static_cast<int>(blockIdx.x) * P + sp + (first + slot) * GP;
-            if (grp < n_out) {
+            if (grp < n_grp) {
                 float tot[NV];
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
@@ -407,7 +426,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     };
 
     auto finish = [&](const u32x4 (&wq)[NV][TW], const ChunkScale (&pp)[NV][TW], int grp, int slot) {
-        if (grp >= n_out) return;   // this stream is past its last group (wave-uniform)
+        if (grp >= n_grp) return;   // this stream is past its last group (wave-uniform)
         float tot[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
@@ -531,7 +550,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     for (int i = 0; i < rounds; ++i) {   // uniform per block
         finish(wbuf, pbuf, g0 + i * GP, slot);
         const int gn = g0 + (i + 1) * GP;
-        if (gn < n_out) issue(wbuf, pbuf, gn);
+        if (gn < n_grp) issue(wbuf, pbuf, gn);
         if constexpr (S > 1) {
             if (++slot == kBatch || i + 1 == rounds) { combine(first, slot); slot = 0; first = i + 1; }
         }
@@ -545,7 +564,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 // Returns false when a wave would need more activations than registers
 // allow, or when the activation row (xb bytes per element) does not fit in
 // the LDS stage.
-struct StreamSplit { int s, tw; };
+struct StreamSplit { int s, tw, nr = 1; };
 
 bool stream_split(int bits, int k, int xb, StreamSplit& out) {
     if (static_cast<int64_t>(k) * xb > kStreamLds) return false;
@@ -561,6 +580,16 @@ bool stream_split(int bits, int k, int xb, StreamSplit& out) {
     return true;
 }
 
+// Outputs per group of a one-row projection's streams (measured on the four
+// MLP shapes and the Qwen3-8B lm_head): two rows for a down projection or a
+// plain projection whose waves hold one K-tile (Llama-3-8B 4-bit down: 12.85
+// against 13.45 us), one otherwise (two rows with two tiles per wave: Qwen3-8B
+// down 12.15 against 11.38 us; two pairs per group for gate/up: 3-6 % slower
+// on every shape).
+inline int stream_rows_per_group(const StreamSplit& sp, bool gate_up) {
+    return !gate_up && sp.tw == 1 && sp.s >= 2 ? 2 : 1;
+}
+
 // Row streams per block (measured): up to 12 waves per block, and at most 4
 // streams when each wave holds a single tile.  At most 12 waves keeps at
 // least 170 VGPRs per wave (three waves per SIMD), more than any split here
@@ -570,18 +599,19 @@ constexpr int stream_rows_per_block(int s, int tw) {
     return tw == 1 && p > 4 ? 4 : p;
 }
 
-template <int BITS, int XDT, int ODT, bool GU, int EPI, int S, int TW>
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR, int S, int TW>
 int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s,
                   const ChainArgs& ch) {
     if constexpr (TW > StreamShape<BITS>::TW_MAX) {
         return static_cast<int>(hipErrorInvalidValue);
     } else {
         constexpr int P = stream_rows_per_block(S, TW);
-        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, EPI>;
+        auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, EPI, NR>;
         const size_t lds = static_cast<size_t>(k) * x_bytes<XDT>();
         const int res = resident_blocks(kern, 64 * S * P, lds);
         if (res <= 0) return static_cast<int>(hipErrorInvalidValue);
-        const int need = (n_out + P - 1) / P;
+        const int groups = (n_out + NR - 1) / NR;
+        const int need = (groups + P - 1) / P;
         const int blocks = need < res ? need : res;
         // MX: the block scales ride in the scale/bias argument (the kernel reads bytes)
         const float* sbp = is_mx(BITS) ? reinterpret_cast<const float*>(w.block_scales) : w.scale_bias;
@@ -591,44 +621,53 @@ int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, 
     }
 }
 
-template <int BITS, int XDT, int ODT, bool GU, int EPI, int S>
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR, int S>
 int run_stream_s(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
                  hipStream_t s, const ChainArgs& ch) {
     switch (tw) {
-        case 1: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 1>(w, x, r, out, n_out, k, s, ch);
-        case 2: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 2>(w, x, r, out, n_out, k, s, ch);
-        case 3: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 3>(w, x, r, out, n_out, k, s, ch);
-        case 4: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 4>(w, x, r, out, n_out, k, s, ch);
-        case 5: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 5>(w, x, r, out, n_out, k, s, ch);
-        case 6: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 6>(w, x, r, out, n_out, k, s, ch);
-        case 7: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 7>(w, x, r, out, n_out, k, s, ch);
-        default: return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 8>(w, x, r, out, n_out, k, s, ch);
+        case 1: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 1>(w, x, r, out, n_out, k, s, ch);
+        case 2: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 2>(w, x, r, out, n_out, k, s, ch);
+        case 3: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 3>(w, x, r, out, n_out, k, s, ch);
+        case 4: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 4>(w, x, r, out, n_out, k, s, ch);
+        case 5: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 5>(w, x, r, out, n_out, k, s, ch);
+        case 6: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 6>(w, x, r, out, n_out, k, s, ch);
+        case 7: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 7>(w, x, r, out, n_out, k, s, ch);
+        default: return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 8>(w, x, r, out, n_out, k, s, ch);
     }
 }
 
-template <int BITS, int XDT, int ODT, bool GU, int EPI, int S>
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR, int S>
 int run_stream_s12(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, int tw,
                    hipStream_t s, const ChainArgs& ch) {
     // splits with up to 5 waves per row use 1 or 2 tiles per wave; anything else
     // is not instantiated and is refused rather than run short
-    if (tw == 1) return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 1>(w, x, r, out, n_out, k, s, ch);
-    if (tw == 2) return run_stream_st<BITS, XDT, ODT, GU, EPI, S, 2>(w, x, r, out, n_out, k, s, ch);
+    if (tw == 1) return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 1>(w, x, r, out, n_out, k, s, ch);
+    if (tw == 2) return run_stream_st<BITS, XDT, ODT, GU, EPI, NR, S, 2>(w, x, r, out, n_out, k, s, ch);
     return static_cast<int>(hipErrorInvalidValue);
+}
+
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR>
+int run_stream_nr(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k,
+                  const StreamSplit& sp, hipStream_t s, const ChainArgs& ch) {
+    switch (sp.s) {
+        case 1: return run_stream_s12<BITS, XDT, ODT, GU, EPI, NR, 1>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 2: return run_stream_s12<BITS, XDT, ODT, GU, EPI, NR, 2>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 3: return run_stream_s12<BITS, XDT, ODT, GU, EPI, NR, 3>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 4: return run_stream_s12<BITS, XDT, ODT, GU, EPI, NR, 4>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 5: return run_stream_s12<BITS, XDT, ODT, GU, EPI, NR, 5>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 6: return run_stream_s<BITS, XDT, ODT, GU, EPI, NR, 6>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        case 7: return run_stream_s<BITS, XDT, ODT, GU, EPI, NR, 7>(w, x, r, out, n_out, k, sp.tw, s, ch);
+        default: return run_stream_s<BITS, XDT, ODT, GU, EPI, NR, 8>(w, x, r, out, n_out, k, sp.tw, s, ch);
+    }
 }
 
 template <int BITS, int XDT, int ODT, bool GU, int EPI>
 int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, const StreamSplit& sp,
                hipStream_t s, const ChainArgs& ch) {
-    switch (sp.s) {
-        case 1: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 1>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 2: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 2>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 3: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 3>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 4: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 4>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 5: return run_stream_s12<BITS, XDT, ODT, GU, EPI, 5>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 6: return run_stream_s<BITS, XDT, ODT, GU, EPI, 6>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        case 7: return run_stream_s<BITS, XDT, ODT, GU, EPI, 7>(w, x, r, out, n_out, k, sp.tw, s, ch);
-        default: return run_stream_s<BITS, XDT, ODT, GU, EPI, 8>(w, x, r, out, n_out, k, sp.tw, s, ch);
+    if constexpr (!GU) {   // two pairs per group measured slower for gate/up: not instantiated
+        if (sp.nr == 2) return run_stream_nr<BITS, XDT, ODT, GU, EPI, 2>(w, x, r, out, n_out, k, sp, s, ch);
     }
+    return run_stream_nr<BITS, XDT, ODT, GU, EPI, 1>(w, x, r, out, n_out, k, sp, s, ch);
 }
 
 }  // namespace
