@@ -26,6 +26,7 @@ int run_chain(const ChainArgs& ch, const qdm_weight& gu, const qdm_weight& dn, f
         return static_cast<int>(hipErrorInvalidValue);
     sg.nr = stream_rows_per_group(sg, true);
     sd.nr = stream_rows_per_group(sd, false);
+    stream_split_down(dn.bits, ffn, sd);
     int e;
     switch (gu.bits) {
         case 8: e = run_stream<8, XDT, DT_F32, true, kEpiChain>(gu, nullptr, nullptr, h, ffn, d, sg, s, ch); break;

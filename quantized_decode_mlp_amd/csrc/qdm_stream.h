@@ -93,6 +93,7 @@ struct StreamShape {
 };
 
 constexpr int kBatch = 16;            // rounds whose split-K partials share one LDS combine
+constexpr bool kDownStageFirst = true;   // stage the fp32 hidden row before the first weight loads
 constexpr int kStreamLds = 65536;     // largest activation row staged in LDS (bytes)
 
 template <int XDT>
@@ -206,6 +207,21 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         }
     };
 
+    // Down (fp32 hidden row): the row is staged completely before the first
+    // weight loads.  A CU returns load data in issue order, so hidden-row
+    // pieces queued behind other waves' weight misses would arrive only as
+    // the HBM queue drains (measured: the staging barrier at 4 us into an
+    // 11 us launch); loaded first they come back from the caches at once.
+    constexpr bool HFIRST = kDownStageFirst && !GU && XDT == DT_F32 && !NORM;
+    if constexpr (HFIRST) {
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int idx = tid + u * NT;
+            if (idx < nunits) xl[idx] = xt[u];
+        }
+        for (int idx = tid + XU * NT; idx < nunits; idx += NT) xl[idx] = xg[idx];
+    }
+
     // the first round goes in flight before the activations are set up
     if (g0 < n_grp) issue(wbuf, pbuf, g0);
 
@@ -256,7 +272,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         };
         if (tid < nunits) norm_piece(tid, wt);
         for (int idx = tid + NT; idx < nunits; idx += NT) norm_piece(idx, wg[idx]);
-    } else {
+    } else if constexpr (!HFIRST) {
         // rest of the activation copy, then this wave's slice
 #pragma unroll
         for (int u = 0; u < XU; ++u) {
@@ -545,15 +561,18 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         }
     };
 
-    // one round in flight per wave: reduce round i, then issue round i + 1
     int slot = 0, first = 0;
+    auto bookkeep = [&](int i) {
+        if constexpr (S > 1) {
+            if (++slot == kBatch || i + 1 == rounds) { combine(first, slot); slot = 0; first = i + 1; }
+        }
+    };
+    // one round in flight per wave: reduce round i, then issue round i + 1
     for (int i = 0; i < rounds; ++i) {   // uniform per block
         finish(wbuf, pbuf, g0 + i * GP, slot);
         const int gn = g0 + (i + 1) * GP;
         if (gn < n_grp) issue(wbuf, pbuf, gn);
-        if constexpr (S > 1) {
-            if (++slot == kBatch || i + 1 == rounds) { combine(first, slot); slot = 0; first = i + 1; }
-        }
+        bookkeep(i);
     }
 }
 
@@ -564,7 +583,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
 // Returns false when a wave would need more activations than registers
 // allow, or when the activation row (xb bytes per element) does not fit in
 // the LDS stage.
-struct StreamSplit { int s, tw, nr = 1; };
+struct StreamSplit { int s, tw, nr = 1, p = 0; };   // p: row streams per block (0: the default rule)
 
 bool stream_split(int bits, int k, int xb, StreamSplit& out) {
     if (static_cast<int64_t>(k) * xb > kStreamLds) return false;
@@ -586,6 +605,24 @@ bool stream_split(int bits, int k, int xb, StreamSplit& out) {
 // against 13.45 us), one otherwise (two rows with two tiles per wave: Qwen3-8B
 // down 12.15 against 11.38 us; two pairs per group for gate/up: 3-6 % slower
 // on every shape).
+// The down projection (fp32 hidden row, staged whole in every block's LDS):
+// four waves per row and four rows per block, i.e. 16-wave blocks and one
+// block per CU, when the row has at least five K-tiles and four waves can
+// hold them.  One staged copy of the hidden row per CU instead of two, and
+// no second block trailing the first (measured, down / layer: Qwen3-8B
+// 11.12 -> 10.89 / 29.17 -> 28.47 us, Llama-3.2-1B 6.50 -> 5.69 / 14.49 ->
+// 14.16, Llama-3-8B 4-bit 11.90 -> 11.92 / 28.25 -> 26.88, Qwen2.5-1.5B
+// dense 7.62 -> 6.86 / 17.16 -> 16.88; other shapes of 16-wave blocks --
+// 3 x 4 tiles, 8 x 1 tile with two rows, two rounds in flight -- were slower).
+inline void stream_split_down(int bits, int k, StreamSplit& sp) {
+    const int cb = code_bits(bits);
+    const int64_t rb = static_cast<int64_t>(k) * cb / 8;
+    const int t = static_cast<int>(((rb >> 4) + 63) >> 6);
+    const int tw_max = cb == 8 ? 4 : cb == 4 ? 2 : 8;
+    const int tw = (t + 3) / 4;
+    if (t >= 5 && tw <= tw_max) sp = StreamSplit{4, tw, 1, 4};
+}
+
 inline int stream_rows_per_group(const StreamSplit& sp, bool gate_up) {
     return !gate_up && sp.tw == 1 && sp.s >= 2 ? 2 : 1;
 }
@@ -601,11 +638,15 @@ constexpr int stream_rows_per_block(int s, int tw) {
 
 template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR, int S, int TW>
 int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s,
-                  const ChainArgs& ch) {
+                  const ChainArgs& ch);
+
+// The launch with P row streams per block (S * P waves).
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR, int S, int TW, int P>
+int run_stream_p(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s,
+                 const ChainArgs& ch) {
     if constexpr (TW > StreamShape<BITS>::TW_MAX) {
         return static_cast<int>(hipErrorInvalidValue);
     } else {
-        constexpr int P = stream_rows_per_block(S, TW);
         auto kern = qgemv_stream_kernel<BITS, XDT, ODT, GU, S, TW, P, EPI, NR>;
         const size_t lds = static_cast<size_t>(k) * x_bytes<XDT>();
         const int res = resident_blocks(kern, 64 * S * P, lds);
@@ -619,6 +660,13 @@ int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, 
                                        static_cast<const uint8_t*>(w.q), sbp, x, r, out, n_out, k,
                                        gshift_of(w.group), ch));
     }
+}
+
+template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR, int S, int TW>
+int run_stream_st(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, hipStream_t s,
+                  const ChainArgs& ch) {
+    return run_stream_p<BITS, XDT, ODT, GU, EPI, NR, S, TW, stream_rows_per_block(S, TW)>(w, x, r, out, n_out,
+                                                                                                 k, s, ch);
 }
 
 template <int BITS, int XDT, int ODT, bool GU, int EPI, int NR, int S>
@@ -665,6 +713,20 @@ template <int BITS, int XDT, int ODT, bool GU, int EPI>
 int run_stream(const qdm_weight& w, const void* x, const void* r, void* out, int n_out, int k, const StreamSplit& sp,
                hipStream_t s, const ChainArgs& ch) {
     if constexpr (!GU) {   // two pairs per group measured slower for gate/up: not instantiated
+        if constexpr (XDT == DT_F32) {   // the down projection's 16-wave blocks
+            if (sp.p == 4 && sp.s == 4) {
+                switch (sp.tw) {
+                    case 2: return run_stream_p<BITS, XDT, ODT, GU, EPI, 1, 4, 2, 4>(w, x, r, out, n_out, k, s, ch);
+                    case 3: return run_stream_p<BITS, XDT, ODT, GU, EPI, 1, 4, 3, 4>(w, x, r, out, n_out, k, s, ch);
+                    case 4: return run_stream_p<BITS, XDT, ODT, GU, EPI, 1, 4, 4, 4>(w, x, r, out, n_out, k, s, ch);
+                    case 5: return run_stream_p<BITS, XDT, ODT, GU, EPI, 1, 4, 5, 4>(w, x, r, out, n_out, k, s, ch);
+                    case 6: return run_stream_p<BITS, XDT, ODT, GU, EPI, 1, 4, 6, 4>(w, x, r, out, n_out, k, s, ch);
+                    case 7: return run_stream_p<BITS, XDT, ODT, GU, EPI, 1, 4, 7, 4>(w, x, r, out, n_out, k, s, ch);
+                    case 8: return run_stream_p<BITS, XDT, ODT, GU, EPI, 1, 4, 8, 4>(w, x, r, out, n_out, k, s, ch);
+                    default: return static_cast<int>(hipErrorInvalidValue);
+                }
+            }
+        }
         if (sp.nr == 2) return run_stream_nr<BITS, XDT, ODT, GU, EPI, 2>(w, x, r, out, n_out, k, sp, s, ch);
     }
     return run_stream_nr<BITS, XDT, ODT, GU, EPI, 1>(w, x, r, out, n_out, k, sp, s, ch);
