@@ -9,12 +9,14 @@ L2s) resident in HBM and rotated per call, 1 activation row in bf16.  One
 step = one MLP layer decode (the gate/up + SwiGLU kernel and the down +
 residual kernel) on layer (step mod 36).
 
-Timed region: W eager warm-up steps, then whole replays of a HIP graph that
-holds one 36-layer rotation, at least --min-rotations of them and enough to
+Timed region: W eager warm-up steps and --warmup-ms of untimed graph
+replays, then whole replays of a HIP graph that holds one 36-layer rotation, at least --min-rotations of them and enough to
 cover K steps; the steps actually timed are reported (`steps_timed`).  The
 time per layer is the HIP-event time of those replays on the launch stream
 divided by the layers they ran; the wall-clock time of the same region,
-bracketed by device synchronizations, is reported beside it.
+bracketed by device synchronizations, is reported beside it, and the
+p10 / p50 / p90 of the region's per-rotation times (events between the
+replays).
 
 Every configuration (the headline stack, the decode chain, the other four
 workloads, the add + RMSNorm rows, the projections, the group, scale/bias and
@@ -452,8 +454,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3600)
     ap.add_argument("--warmup", type=int, default=108)
-    ap.add_argument("--min-rotations", type=int, default=5,
+    ap.add_argument("--min-rotations", type=int, default=20,
                     help="whole 36-layer rotations timed at least (the timed steps round up to these)")
+    ap.add_argument("--warmup-ms", type=float, default=500.0,
+                    help="untimed graph replays before the timed region (milliseconds)")
     ap.add_argument("--event-launches", type=int, default=720)
     ap.add_argument("--cpu-layers", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -501,7 +505,9 @@ def main(argv=None):
     def step(i):
         qdm.mlp_decode(xd, rd, *sets[i % n_layers], workspace=ws, out=out)
 
-    # ---- the timed region: W eager steps, then whole rotations of one graph
+    # ---- the timed region: W eager steps and, untimed, graph replays for
+    # --warmup-ms (the GPU leaves its idle clocks during the host-side
+    # preparation only once it is kept busy), then whole rotations of the graph
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -511,18 +517,24 @@ def main(argv=None):
             step(i)
     g.replay()
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < args.warmup_ms * 1e-3:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
     rotations = max(args.min_rotations, -(-args.steps // n_layers))
     steps_timed = rotations * n_layers
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(rotations + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    a.record()
-    for _ in range(rotations):
+    ev[0].record()
+    for j in range(rotations):
         g.replay()
-    b.record()
+        ev[j + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    us = a.elapsed_time(b) * 1e3 / steps_timed
+    us = ev[0].elapsed_time(ev[-1]) * 1e3 / steps_timed
+    rotation_us = [ev[j].elapsed_time(ev[j + 1]) * 1e3 / n_layers for j in range(rotations)]
     us_wall = wall * 1e6 / steps_timed
     gbps = wl.weight_bytes / (us * 1e-6) / 1e9
     _log(f"headline: {us:.3f} us/layer over {steps_timed} steps ({us_wall:.3f} us by the wall clock)")
@@ -559,7 +571,7 @@ def main(argv=None):
     _log(f"{len(cases)} configurations captured; sampling")
     sample_interleaved(cases, args.samples)
     recs = {c.name: c.record() for c in cases}
-    spread = recs.pop("headline")["us_per_layer"]
+    interleaved = recs.pop("headline")["us_per_layer"]
     chain = {"workload": "Qwen3-8B-shaped layer as above, with the residual add + RMSNorm (bf16, eps 1e-5) "
                          "that feeds it",
              "add_rmsnorm_then_mlp": recs.pop("decode_chain/add_rmsnorm_then_mlp"),
@@ -598,7 +610,9 @@ def main(argv=None):
                       f"({steps_timed} steps, HIP events on the launch stream)",
         },
         "wall_us_per_layer": round(us_wall, 3),
-        "us_per_layer_samples": spread,
+        "us_per_layer_samples": pcts(rotation_us),
+        "samples": f"per-rotation times of the timed region ({rotations} rotations of {n_layers} layers)",
+        "interleaved_us_per_layer": interleaved,
         "kernels_us": {"gemv_gate_up_swiglu": round(gu_us, 3), "gemv_down_residual": round(dn_us, 3)},
         "roofline": {
             "kernel": "gemv_gate_up_swiglu",

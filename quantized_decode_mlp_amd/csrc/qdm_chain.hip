@@ -25,6 +25,7 @@ int run_chain(const ChainArgs& ch, const qdm_weight& gu, const qdm_weight& dn, f
     if (!stream_split(gu.bits, d, x_bytes<XDT>(), sg) || !stream_split(dn.bits, ffn, 4, sd))
         return static_cast<int>(hipErrorInvalidValue);
     sg.nr = stream_rows_per_group(sg, true);
+    stream_split_gate_up(gu.bits, sg);
     sd.nr = stream_rows_per_group(sd, false);
     stream_split_down(dn.bits, ffn, sd);
     int e;

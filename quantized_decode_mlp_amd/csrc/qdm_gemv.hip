@@ -219,6 +219,7 @@ int run_rows(const qdm_weight& w, const void* x, int64_t x_row, const void* r, v
         if (stream_split(w.bits, k, x_bytes<XDT>(), sp)) {
             sp.nr = stream_rows_per_group(sp, GU);
             if (!GU && XDT == DT_F32) stream_split_down(w.bits, k, sp);
+            if (GU) stream_split_gate_up(w.bits, sp);
             switch (w.bits) {
                 case 8: return run_stream<8, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
                 case 4: return run_stream<4, XDT, ODT, GU, kEpiPlain>(w, x, r, out, n_out, k, sp, s, ChainArgs{});
