@@ -75,6 +75,16 @@ __device__ __forceinline__ uint32_t dword_map(uint32_t xa, uint32_t xb, F f) {
     }
 }
 
+// The sum-of-squares order of add + RMSNorm, shared by the standalone kernel
+// and the decode chain's gate/up prologues (which must reproduce its n bit for
+// bit): thread t of kNormThreads takes the 16-byte chunks t, t + kNormThreads,
+// ... of the row (norm_chunk<DT> elements each) and accumulates the squares of
+// their elements in index order with fmaf; the lanes of each wave are then
+// summed by wave_total and the kNormThreads / 64 wave sums in wave order.
+constexpr int kNormThreads = 256;
+template <int DT>
+__host__ __device__ constexpr int norm_chunk() { return DT == DT_F32 ? 4 : 8; }
+
 // Loads N consecutive elements (N * sizeof(elem) in {4, 8, 16, 32} bytes, aligned
 // to min(16, that size)) as fp32.
 template <int DT, int N>

@@ -70,7 +70,6 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
     constexpr int KBK = L::KBK, STEPS = L::STEPS, NF = L::NF, FG = L::FG;
     constexpr bool WIDE = L::WIDE;
     constexpr int CPF = FG / 8;   // 16-byte activation pieces per fold chunk
-    constexpr int kNormThreads = 256;   // the standalone add + RMSNorm kernel's block
     static_assert(!NORM || NT % kNormThreads == 0, "the norm prologue takes rows in 256-thread groups");
 
     extern __shared__ __align__(16) uint8_t lds[];
@@ -233,10 +232,10 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         // The decode chain's RMSNorm per row, recomputed by every block: s =
         // a + b rounded once, staged as is (block 0 also stores it for the
         // down projection's residual); each row's mean square summed exactly
-        // as the standalone add + RMSNorm kernel sums it (its 256 threads'
-        // strided sums, wave sums, the four in order; rows in 256-thread
-        // groups); then n = s * inv * w rounded once goes through stage_piece
-        // in place.  n is the value that kernel would store.
+        // as the standalone add + RMSNorm kernel sums it (norm_chunk /
+        // kNormThreads order; rows in 256-thread groups); then n = s * inv * w
+        // rounded once goes through stage_piece in place.  n is the value that
+        // kernel would store.
         const int tid = static_cast<int>(threadIdx.x);
         u32x4* sg = static_cast<u32x4*>(na.s_buf);
         auto sum_piece = [&](int u, const u32x4 av, const u32x4 bv) {
@@ -256,14 +255,18 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         for (int u = XPT * NT + tid; u < npieces; u += NT) sum_piece(u, xg[u], bg[u]);
         __syncthreads();
         const int t = tid & (kNormThreads - 1);
+        constexpr int CE = norm_chunk<XDT>();
         for (int m = tid / kNormThreads; m < m_rows; m += NT / kNormThreads) {
             float ss = 0.f;
-            for (int i = t; i < K; i += kNormThreads) {
-                const uint32_t e = xs[m * ldx + i];
-                const float v = XDT == DT_BF16 ? bf16_to_f32(e) : f16_to_f32(e);
-                ss = fmaf(v, v, ss);
+            for (int c = t; c * CE < K; c += kNormThreads) {   // the standalone kernel's order
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    const uint32_t h = xs[m * ldx + c * CE + e];
+                    const float v = XDT == DT_BF16 ? bf16_to_f32(h) : f16_to_f32(h);
+                    ss = fmaf(v, v, ss);
+                }
             }
-            ss = wave_sum(ss);
+            ss = wave_total(ss);
             if ((t & 63) == 0) nred[m][t >> 6] = ss;
         }
         __syncthreads();

@@ -123,7 +123,6 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     constexpr int NT = 64 * S * P;
     constexpr int XU = 4;   // 16-byte activation pieces per thread loaded ahead of the first weights
     constexpr bool NORM = EPI == kEpiChain && GU;   // the activation row is rmsnorm(a + b) * w
-    constexpr int kNormThreads = 256;    // the standalone add + RMSNorm kernel's block
     static_assert(!NORM || NT >= kNormThreads, "the norm prologue needs four waves");
 
     extern __shared__ __align__(16) uint8_t xlds[];   // the activation row, k * x_bytes bytes
@@ -230,9 +229,9 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         // The decode chain's RMSNorm, recomputed by every block from a, b and w
         // (L2-resident after the first blocks): s = a + b rounded once, staged
         // in LDS; the mean square of s summed exactly as the standalone add +
-        // RMSNorm kernel does (its 256 threads' strided sums, wave sums, the
-        // four in order); then n = s * inv * w rounded once, in place.  n is
-        // therefore the value that kernel would store.
+        // RMSNorm kernel does (norm_chunk / kNormThreads order); then
+        // n = s * inv * w rounded once, in place.  n is therefore the value
+        // that kernel would store.
         const u32x4* bg = static_cast<const u32x4*>(ch.b);
         const u32x4* wg = static_cast<const u32x4*>(ch.w);
         auto add_piece = [&](int idx, const u32x4 av, const u32x4 bv) {
@@ -248,12 +247,19 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         for (int idx = tid + NT; idx < nunits; idx += NT) add_piece(idx, xg[idx], bg[idx]);
         __syncthreads();
         if (tid < kNormThreads) {
+            // the standalone kernel's order: chunks tid, tid + kNormThreads, ...
+            constexpr int CE = norm_chunk<XDT>();
             float ss = 0.f;
-            for (int i = tid; i < k; i += kNormThreads) {
-                const float sv = load_elem<XDT>(xlds, i);
-                ss = fmaf(sv, sv, ss);
+            for (int c = tid; c * CE < k; c += kNormThreads) {
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    if (c * CE + e < k) {
+                        const float sv = load_elem<XDT>(xlds, c * CE + e);
+                        ss = fmaf(sv, sv, ss);
+                    }
+                }
             }
-            ss = wave_sum(ss);
+            ss = wave_total(ss);
             if ((tid & 63) == 0) nred[tid >> 6] = ss;
         }
         __syncthreads();
