@@ -235,67 +235,89 @@ def headline_cases(sets, wl):
     return cases
 
 
-def workload_cases():
+def _everything(name):
+    return True
+
+
+def workload_cases(want=_everything):
     """Workloads 1, 2, 3 and 5 (5 at 1, 4, 16 rows and at 128 and 512 rows on
-    the tiled kernels), and the add + RMSNorm rows of workloads 1 and 2."""
+    the tiled kernels), and the add + RMSNorm rows of workloads 1 and 2 (only
+    the configurations `want` accepts)."""
     import torch
     import quantized_decode_mlp_amd as qdm
     cases = []
     # workload 1: 0.49 MB of weights stay cache-resident; launch-bound by design
-    wl = W.WORKLOADS[1]
-    sets, nbytes = packed_copies(wl, copies=36)
-    cases.append(mlp_case("workload1_m1", wl, sets, nbytes, 1,
-                          info={"copies": 36, "note": "0.49 MB of weights: cache-resident, launch-bound"}))
+    if want("workload1_m1"):
+        wl = W.WORKLOADS[1]
+        sets, nbytes = packed_copies(wl, copies=36)
+        cases.append(mlp_case("workload1_m1", wl, sets, nbytes, 1,
+                              info={"copies": 36, "note": "0.49 MB of weights: cache-resident, launch-bound"}))
     for wi in (1, 2):
         wl = W.WORKLOADS[wi]
+        name = f"add_rmsnorm_{wl.norm_dtype}_{wl.d}"
+        if not want(name):
+            continue
         a, b, w = W.rmsnorm_inputs(wl)
         ad, bd, wd = _dev(a), _dev(b), _dev(w)
         so, no = torch.empty_like(ad), torch.empty_like(ad)
-        name = f"add_rmsnorm_{wl.norm_dtype}_{wl.d}"
         cases.append(Case(name, lambda i: qdm.add_rmsnorm(ad, bd, wd, wl.norm_eps, s_out=so, n_out=no), 36,
                           keep=(ad, bd, wd, so, no)))
     for wi in (2, 3, 5):
         wl = W.WORKLOADS[wi]
+        rows = [m for m in (wl.rows + (128, 512) if wi == 5 else (1,)) if want(f"workload{wi}_m{m}")]
+        if not rows:
+            continue
         sets, nbytes = packed_copies(wl)
-        for m in (wl.rows + (128, 512) if wi == 5 else (1,)):
+        for m in rows:
             cases.append(mlp_case(f"workload{wi}_m{m}", wl, sets, nbytes, m))
             _log(f"captured workload {wi} m={m}")
-    z = torch.empty(1, device="cuda")
-    cases.append(Case("launch_floor_fill_kernel", lambda i: z.zero_(), 36, keep=(z,)))
+    if want("launch_floor_fill_kernel"):
+        z = torch.empty(1, device="cuda")
+        cases.append(Case("launch_floor_fill_kernel", lambda i: z.zero_(), 36, keep=(z,)))
     return cases
 
 
-def variant_cases():
+def variant_cases(want=_everything):
     """The one-row MLP of each quantized shape at groups 32/64/128; the affine
     formats with bf16 (scale, bias) pairs; MXFP8 / MXFP4 weights."""
     cases = []
     for wi in (2, 4, 5):
         wl = W.WORKLOADS[wi]
         for group in (32, 64, 128):
-            sets, nbytes = packed_copies(wl, group=group)
-            cases.append(mlp_case(f"group_sweep/workload{wi}_m1/g{group}", wl, sets, nbytes, 1))
-        sets, nbytes = packed_copies(wl, fmt="sb16")
-        for m in ((1, 4, 16) if wi == 5 else (1,)):
-            cases.append(mlp_case(f"bf16_scale_bias/workload{wi}_m{m}", wl, sets, nbytes, m))
+            name = f"group_sweep/workload{wi}_m1/g{group}"
+            if want(name):
+                sets, nbytes = packed_copies(wl, group=group)
+                cases.append(mlp_case(name, wl, sets, nbytes, 1))
+        rows = [m for m in ((1, 4, 16) if wi == 5 else (1,)) if want(f"bf16_scale_bias/workload{wi}_m{m}")]
+        if rows:
+            sets, nbytes = packed_copies(wl, fmt="sb16")
+            for m in rows:
+                cases.append(mlp_case(f"bf16_scale_bias/workload{wi}_m{m}", wl, sets, nbytes, m))
         _log(f"captured variants of workload {wi}")
     wl = W.WORKLOADS[4]
     for fmt in ("mxfp8", "mxfp4"):
-        sets, nbytes = packed_copies(wl, fmt=fmt)
-        cases.append(mlp_case(f"qwen3_8b_{fmt}_m1", wl, sets, nbytes, 1))
+        if want(f"qwen3_8b_{fmt}_m1"):
+            sets, nbytes = packed_copies(wl, fmt=fmt)
+            cases.append(mlp_case(f"qwen3_8b_{fmt}_m1", wl, sets, nbytes, 1))
     wl = W.WORKLOADS[5]
-    sets, nbytes = packed_copies(wl, fmt="mxfp4")
-    for m in wl.rows:
-        cases.append(mlp_case(f"llama3_8b_mxfp4_m{m}", wl, sets, nbytes, m))
+    rows = [m for m in wl.rows if want(f"llama3_8b_mxfp4_m{m}")]
+    if rows:
+        sets, nbytes = packed_copies(wl, fmt="mxfp4")
+        for m in rows:
+            cases.append(mlp_case(f"llama3_8b_mxfp4_m{m}", wl, sets, nbytes, m))
     return cases
 
 
-def projection_cases():
+def projection_cases(want=_everything):
     """One-row projections other than the MLP: the Qwen3-8B-shaped lm_head (vocab
     151936), and the attention projections of a Qwen2.5-1.5B-shaped layer (q/k/v
     with bias, o without) in four launches and with q/k/v stacked in two."""
     import torch
     import quantized_decode_mlp_amd as qdm
     cases = []
+    if not (want("lm_head_qwen3_8b") or want("attention_qkvo_qwen25_1p5b")
+            or want("attention_fused_qkv_o_qwen25_1p5b")):
+        return cases
 
     def prepared(p):
         w32, b, x = W.projection_inputs(p, 1)
@@ -447,6 +469,18 @@ def cpu_baseline(wl: W.Workload, layers: int):
     }
 
 
+def calibration_copy():
+    """A plain 256 MiB device-to-device copy, three times: its FETCH_SIZE / WRITE_SIZE
+    readings give the counters' scale."""
+    import torch
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 # ------------------------------------------------------------------ main
 
 def main(argv=None):
@@ -485,12 +519,18 @@ def main(argv=None):
 
     if args.only:
         wanted = [s for s in args.only.split(",") if s]
+
+        def want(name):
+            return any(name.startswith(w) for w in wanted)
+
         builders = (workload_cases, variant_cases, projection_cases)
-        cases = [c for b in builders for c in b() if any(c.name.startswith(w) for w in wanted)]
+        cases = [c for b in builders for c in b(want) if want(c.name)]
         if not cases:
             print(json.dumps({"error": f"no configuration matches {args.only!r}"}))
             return 2
         sample_interleaved(cases, args.samples)
+        if args.calibration_copy:
+            calibration_copy()
         print(json.dumps({"only": args.only, "configs": {c.name: c.record() for c in cases}}), flush=True)
         return 0
 
@@ -556,13 +596,7 @@ def main(argv=None):
     finite = bool(torch.isfinite(y_dev.float()).all())
 
     if args.calibration_copy:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE give the counters' scale
-        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy()
 
     # ---- every configuration, sampled in interleaved rounds
     cases = headline_cases(sets, wl)
