@@ -241,7 +241,8 @@ def _everything(name):
 
 def workload_cases(want=_everything):
     """Workloads 1, 2, 3 and 5 (5 at 1, 4, 16 rows and at 128 and 512 rows on
-    the tiled kernels), and the add + RMSNorm rows of workloads 1 and 2 (only
+    the tiled kernels), the add + RMSNorm rows of workloads 1 and 2 and of the
+    Qwen3-8B decode chain (only
     the configurations `want` accepts)."""
     import torch
     import quantized_decode_mlp_amd as qdm
@@ -252,12 +253,14 @@ def workload_cases(want=_everything):
         sets, nbytes = packed_copies(wl, copies=36)
         cases.append(mlp_case("workload1_m1", wl, sets, nbytes, 1,
                               info={"copies": 36, "note": "0.49 MB of weights: cache-resident, launch-bound"}))
-    for wi in (1, 2):
+    for wi in (1, 2, 4):
+        # workload 4 has no standalone add + RMSNorm: its decode chain's norm
+        # (the MLP's bf16 activations, d = 4096) stands in
         wl = W.WORKLOADS[wi]
-        name = f"add_rmsnorm_{wl.norm_dtype}_{wl.d}"
+        name = f"add_rmsnorm_{wl.norm_dtype or wl.act}_{wl.d}"
         if not want(name):
             continue
-        a, b, w = W.rmsnorm_inputs(wl)
+        a, b, w = W.rmsnorm_inputs(wl) if wl.norm_dtype else W.chain_inputs(wl)
         ad, bd, wd = _dev(a), _dev(b), _dev(w)
         so, no = torch.empty_like(ad), torch.empty_like(ad)
         cases.append(Case(name, lambda i: qdm.add_rmsnorm(ad, bd, wd, wl.norm_eps, s_out=so, n_out=no), 36,
@@ -498,8 +501,9 @@ def main(argv=None):
     ap.add_argument("--samples", type=int, default=20, help="interleaved sampling rounds")
     ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma-separated configuration names (or prefixes, e.g. workload5_m,group_sweep/): "
-                         "capture and sample only those, skip the headline, print their records")
+                    help="comma-separated configuration names, or prefixes ending in '*' "
+                         "(e.g. workload5_m*,group_sweep/*): capture and sample only those, skip the "
+                         "headline, print their records")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args(argv)
@@ -521,7 +525,7 @@ def main(argv=None):
         wanted = [s for s in args.only.split(",") if s]
 
         def want(name):
-            return any(name.startswith(w) for w in wanted)
+            return any(name.startswith(w[:-1]) if w.endswith("*") else name == w for w in wanted)
 
         builders = (workload_cases, variant_cases, projection_cases)
         cases = [c for b in builders for c in b(want) if want(c.name)]

@@ -146,38 +146,70 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
     const int ppr = KR / 8;
     const int npieces = m_rows * ppr;
     auto pack2 = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
-    for (int u0 = 0; u0 < npieces; u0 += 64 * S * P) {
-        const int u = u0 + static_cast<int>(threadIdx.x);
-        float sum = 0.f;
-        int m = 0, c = 0;
-        if (u < npieces) {
-            m = u / ppr;
-            c = u - m * ppr;
+    // two pieces per thread at a time, both loaded (at clamped indices) before
+    // either is staged: one wait per pair of pieces
+    constexpr int HB = 2;
+    constexpr int NT = 64 * S * P;
+    f32x4 ld[HB][2];
+    auto load_batch = [&](int u0) {
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+            const int u = min(u0 + j * NT + static_cast<int>(threadIdx.x), npieces - 1);
+            const int m = u / ppr, c = u - m * ppr;
             const f32x4* src = reinterpret_cast<const f32x4*>(h + static_cast<size_t>(m) * K + ksl * KR + c * 8);
-            const f32x4 a0 = src[0], a1 = src[1];
-            uint32_t hi[8], lo[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = e < 4 ? a0[e] : a1[e - 4];
-                hi[e] = __float_as_uint(v) & 0xffff0000u;   // truncation: the exact top half
-                const float rem = v - __uint_as_float(hi[e]);
-                lo[e] = __float_as_uint(rem) & 0xffff0000u;
-                sum += __uint_as_float(hi[e]) + __uint_as_float(lo[e]);
-            }
-            u32x4 oh, ol;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // element pairs (2i, 2i+1), or (i, i+4) for 4-bit codes
-                const int ea = nibble_pairs(BITS) ? i : 2 * i, eb = nibble_pairs(BITS) ? i + 4 : 2 * i + 1;
-                oh[i] = pack2(hi[ea], hi[eb]);
-                ol[i] = pack2(lo[ea], lo[eb]);
-            }
-            *reinterpret_cast<u32x4*>(xh + m * ldx + c * 8) = oh;
-            *reinterpret_cast<u32x4*>(xl + m * ldx + c * 8) = ol;
+            ld[j][0] = src[0];
+            ld[j][1] = src[1];
         }
+    };
+    auto stage_batch = [&](int u0) {
 #pragma unroll
-        for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
-        if (u < npieces && c % CPF == 0) xsum[(c / CPF) * kRows + m] = sum;
+        for (int j = 0; j < HB; ++j) {
+            const int u = u0 + j * NT + static_cast<int>(threadIdx.x);
+            float sum = 0.f;
+            int m = 0, c = 0;
+            if (u < npieces) {
+                m = u / ppr;
+                c = u - m * ppr;
+                const f32x4 a0 = ld[j][0], a1 = ld[j][1];
+                uint32_t hi[8], lo[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = e < 4 ? a0[e] : a1[e - 4];
+                    hi[e] = __float_as_uint(v) & 0xffff0000u;   // truncation: the exact top half
+                    const float rem = v - __uint_as_float(hi[e]);
+                    lo[e] = __float_as_uint(rem) & 0xffff0000u;
+                    sum += __uint_as_float(hi[e]) + __uint_as_float(lo[e]);
+                }
+                u32x4 oh, ol;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // element pairs (2i, 2i+1), or (i, i+4) for 4-bit codes
+                    const int ea = nibble_pairs(BITS) ? i : 2 * i, eb = nibble_pairs(BITS) ? i + 4 : 2 * i + 1;
+                    oh[i] = pack2(hi[ea], hi[eb]);
+                    ol[i] = pack2(lo[ea], lo[eb]);
+                }
+                *reinterpret_cast<u32x4*>(xh + m * ldx + c * 8) = oh;
+                *reinterpret_cast<u32x4*>(xl + m * ldx + c * 8) = ol;
+            }
+#pragma unroll
+            for (int o2 = 1; o2 < CPF; o2 <<= 1) sum += __shfl_xor(sum, o2, 64);
+            if (u < npieces && c % CPF == 0) xsum[(c / CPF) * kRows + m] = sum;
+        }
+    };
+    load_batch(0);
+    // The first round's pairs and code loads go out behind the first h loads
+    // of every wave (an execution barrier only: nothing is waited for), so
+    // the weight stream starts while the slice is staged, and no wave's h
+    // pieces queue behind another wave's weight misses (a CU returns load data
+    // in issue order).
+    __builtin_amdgcn_s_barrier();
+    if (t0 < ntiles) load_pairs(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) issue(st[u], 0, u);
+    stage_batch(0);
+    for (int u0 = HB * NT; u0 < npieces; u0 += HB * NT) {   // uniform
+        load_batch(u0);
+        stage_batch(u0);
     }
     for (int u = static_cast<int>(threadIdx.x); u < (KR / FG) * (kRows - m_rows); u += 64 * S * P) {
         const int ch = u / (kRows - m_rows), m = m_rows + (u - ch * (kRows - m_rows));
@@ -252,9 +284,11 @@ qmm_down_part_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb
     // flight; compute runs only inside the range, the loads on every path
     for (int i = 0; i < rounds; ++i) {   // uniform per block
         const bool live = t0 + i * GP < ntiles;   // wave-uniform
-        if (live) load_pairs(i);
+        if (i > 0) {   // round 0's loads went out before the staging
+            if (live) load_pairs(i);
 #pragma unroll
-        for (int u = 0; u < U; ++u) issue(st[u], i, u);
+            for (int u = 0; u < U; ++u) issue(st[u], i, u);
+        }
         for (int j0 = 0; j0 < nkw; j0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {

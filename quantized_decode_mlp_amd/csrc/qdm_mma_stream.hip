@@ -187,6 +187,13 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
         }
     };
 
+    // Every wave has issued its activation pieces before any weight load goes
+    // out (an execution barrier only: nothing is waited for).  A CU returns
+    // load data in issue order, so pieces issued behind another wave's weight
+    // misses would hold the staging barrier until those drain (Llama-3-8B
+    // 4-bit, 16 rows: 47.8 -> 45.8 us per layer with the down kernel's
+    // matching order).
+    __builtin_amdgcn_s_barrier();
     load_pairs(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) issue(st[u], 0, u);
@@ -291,11 +298,16 @@ qmm_gate_up_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict
             stage_piece(u, nv);
         }
     } else {
+        const int tid = static_cast<int>(threadIdx.x);
 #pragma unroll
-        for (int j = 0; j < XPT; ++j) stage_piece(static_cast<int>(threadIdx.x) + j * NT, xt[j]);
-        for (int u0 = XPT * NT; u0 < npieces; u0 += NT) {
-            const int u = u0 + static_cast<int>(threadIdx.x);
-            stage_piece(u, u < npieces ? xg[u] : u32x4{0u, 0u, 0u, 0u});
+        for (int j = 0; j < XPT; ++j) stage_piece(tid + j * NT, xt[j]);
+        // longer rows: XPT more pieces per thread at a time, all loaded (at
+        // clamped indices) before any is staged, so a batch costs one wait
+        for (int u0 = XPT * NT; u0 < npieces; u0 += XPT * NT) {   // uniform
+#pragma unroll
+            for (int j = 0; j < XPT; ++j) xt[j] = xg[min(u0 + j * NT + tid, npieces - 1)];
+#pragma unroll
+            for (int j = 0; j < XPT; ++j) stage_piece(u0 + j * NT + tid, xt[j]);
         }
     }
     if constexpr (!mx_bits(BITS)) {

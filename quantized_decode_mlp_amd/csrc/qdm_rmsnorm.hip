@@ -11,10 +11,13 @@
 // square of the rounded s is accumulated in fp32 in the fixed order that
 // norm_chunk / kNormThreads define (the one-row and few-row decode chains'
 // gate/up prologues repeat it, so their n is bitwise this kernel's).  Rows of
-// up to kNormThreads * kHeld chunks take one pass: each thread's a, b and w
-// chunks are loaded at once (16 bytes per load when the row length allows),
-// s stays in registers, and n = s * w / sqrt(mean + eps), rounded once, is
-// stored with s.  Longer rows recompute s in a second pass.
+// up to kNormThreads * kHeld chunks take one pass: each thread's H chunks of
+// a, b and w are loaded at once (16 bytes per load when the row length
+// allows; H = the row's chunks / kNormThreads rounded up, a template
+// argument, and every load issued unconditionally at a clamped chunk index,
+// since a load inside a branch ends the branch with a wait for it), s stays in
+// registers, and n = s * w / sqrt(mean + eps), rounded once, is stored with
+// s.  Longer rows recompute s in a second pass.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -81,7 +84,8 @@ __device__ __forceinline__ void store_chunk(void* p, int64_t base, int c, int n,
     }
 }
 
-template <int DT, bool VEC, bool ONE_PASS>
+// H: chunks per thread held in registers (one pass), or 0 (two passes).
+template <int DT, bool VEC, int H>
 __global__ void __launch_bounds__(kThreads)
 add_rmsnorm_kernel(const void* a, const void* b, const void* __restrict__ w,
                    int n, float eps, void* s_out, void* __restrict__ n_out) {
@@ -98,26 +102,24 @@ add_rmsnorm_kernel(const void* a, const void* b, const void* __restrict__ w,
         }
     };
     float ss = 0.f;
-    if constexpr (ONE_PASS) {
-        float sv[kHeld][CE], wv[kHeld][CE];
+    if constexpr (H > 0) {
+        float sv[H][CE], wv[H][CE];
         {
-            float av[kHeld][CE], bv[kHeld][CE];
+            float av[H][CE], bv[H][CE];
 #pragma unroll
-            for (int j = 0; j < kHeld; ++j) {   // every load in flight together
-                const int c = t + j * kThreads;
-                if (c < nch) {
-                    load_chunk<DT, VEC>(a, base, c, n, av[j]);
-                    load_chunk<DT, VEC>(b, base, c, n, bv[j]);
-                    load_chunk<DT, VEC>(w, 0, c, n, wv[j]);
-                }
+            for (int j = 0; j < H; ++j) {   // every load in flight together
+                const int c = min(t + j * kThreads, nch - 1);
+                load_chunk<DT, VEC>(a, base, c, n, av[j]);
+                load_chunk<DT, VEC>(b, base, c, n, bv[j]);
+                load_chunk<DT, VEC>(w, 0, c, n, wv[j]);
             }
 #pragma unroll
-            for (int j = 0; j < kHeld; ++j)
+            for (int j = 0; j < H; ++j)
                 if (t + j * kThreads < nch) sum_chunk(av[j], bv[j], sv[j], t + j * kThreads, ss);
         }
         const float inv = 1.0f / sqrtf(block_sum(ss) / static_cast<float>(n) + eps);
 #pragma unroll
-        for (int j = 0; j < kHeld; ++j) {
+        for (int j = 0; j < H; ++j) {
             const int c = t + j * kThreads;
             if (c < nch) {
                 float nv[CE];
@@ -154,9 +156,16 @@ template <int DT, bool VEC>
 int run_v(const void* a, const void* b, const void* w, int rows, int n, float eps, void* s_out, void* n_out,
           hipStream_t s) {
     const dim3 grid(rows), block(kThreads);
-    if (n <= kThreads * kHeld * norm_chunk<DT>())
-        return launch(add_rmsnorm_kernel<DT, VEC, true>, grid, block, 0, s, a, b, w, n, eps, s_out, n_out);
-    return launch(add_rmsnorm_kernel<DT, VEC, false>, grid, block, 0, s, a, b, w, n, eps, s_out, n_out);
+    static_assert(kHeld == 4, "one-pass instances for 1..4 chunks per thread");
+    const int nch = (n + norm_chunk<DT>() - 1) / norm_chunk<DT>();
+    switch ((nch + kThreads - 1) / kThreads) {
+        case 0:
+        case 1: return launch(add_rmsnorm_kernel<DT, VEC, 1>, grid, block, 0, s, a, b, w, n, eps, s_out, n_out);
+        case 2: return launch(add_rmsnorm_kernel<DT, VEC, 2>, grid, block, 0, s, a, b, w, n, eps, s_out, n_out);
+        case 3: return launch(add_rmsnorm_kernel<DT, VEC, 3>, grid, block, 0, s, a, b, w, n, eps, s_out, n_out);
+        case 4: return launch(add_rmsnorm_kernel<DT, VEC, 4>, grid, block, 0, s, a, b, w, n, eps, s_out, n_out);
+        default: return launch(add_rmsnorm_kernel<DT, VEC, 0>, grid, block, 0, s, a, b, w, n, eps, s_out, n_out);
+    }
 }
 
 template <int DT>

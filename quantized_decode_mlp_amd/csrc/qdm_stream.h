@@ -79,6 +79,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
 
+// Half h (0: bits 0-15, 1: bits 16-31) of w as an f16 value widened to fp32;
+// as an FMA operand the widening folds into v_fma_mix_f32.  A 16-bit field
+// below 0x400 is the subnormal field * 2^-24 (the kernels keep f16
+// subnormals: the default denormal mode).
+__device__ __forceinline__ float f16_half(uint32_t w, int h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h ? w >> 16 : w)));
+}
+
 // BITS is the weight format: 4 / 8 (affine), 16 (dense bf16), QDM_U4_SB16 /
 // QDM_U8_SB16 (affine, bf16 pairs), QDM_MXFP4 / QDM_MXFP8 (block-scaled);
 // the low byte is the code width.
@@ -290,7 +298,8 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     }
     __syncthreads();
 
-    // Dot-product form.  DM 0: fp32 activations, one FMA per code.  DM 1
+    // Dot-product form.  DM 0: fp32 activations, one FMA per code (4-bit codes
+    // enter the mixed-precision FMA as f16 halves; see finish()).  DM 1
     // (8/4-bit codes, 16-bit activations): v_dot2_f32_f16 on two codes at a
     // time.  A code becomes an exact f16 value by placing its bits in the
     // mantissa under a fixed exponent: an 8-bit code c under the exponent
@@ -448,6 +457,12 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         __syncthreads();
     };
 
+    // DM 1, 4-bit: the nibble mask lives in a register, so that each pair of
+    // codes takes one v_and_or_b32 after its shift (with both constants as
+    // literals the compiler splits it into an and and an or)
+    uint32_t nmask = 0x03c003c0u;
+    if constexpr (DM == 1 && CB == 4) asm volatile("" : "+v"(nmask));
+
     auto finish = [&](const u32x4 (&wq)[NV][TW], const ChunkScale (&pp)[NV][TW], int grp, int slot) {
         if (grp >= n_grp) return;   // this stream is past its last group (wave-uniform)
         float tot[NV];
@@ -472,7 +487,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                         for (int e = 0; e < 4; ++e) {
                             // nibbles e and e + 4 into mantissa bits 9..6 of the two halves
                             const uint32_t sh = e < 2 ? word << (6 - 4 * e) : word >> (4 * e - 6);
-                            const uint32_t ce = (sh & 0x03c003c0u) | 0x3c003c00u;
+                            const uint32_t ce = (sh & nmask) | 0x3c003c00u;
                             dot = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, ce),
                                                          __builtin_bit_cast(h16x2, xp[j][4 * i + e]), dot, false);
                         }
@@ -519,12 +534,22 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                         dot = fmaf(f2.y, xv[j][8 * i + 5], dot);
                         dot = fmaf(f3.x, xv[j][8 * i + 6], dot);
                         dot = fmaf(f3.y, xv[j][8 * i + 7], dot);
+                    } else if constexpr (CB == 4) {
+                        // DM 0, 4-bit: nibbles e and e + 4 become the f16 subnormals
+                        // n * 2^-24 of one word's halves (a shift and an and per two
+                        // codes); the mixed-precision FMA multiplies an f16 half with
+                        // an fp32 activation exactly, and 2^24 goes into the scale
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t pr = (word >> (4 * e)) & 0x000f000fu;
+                            dot = fmaf(xv[j][i * 8 + e], f16_half(pr, 0), dot);
+                            dot = fmaf(xv[j][i * 8 + e + 4], f16_half(pr, 1), dot);
+                        }
                     } else {
 #pragma unroll
                         for (int e = 0; e < EPD; ++e) {
                             float c;
                             if constexpr (CB == 8) c = static_cast<float>((word >> (8 * e)) & 0xffu);
-                            else if constexpr (CB == 4) c = static_cast<float>((word >> (4 * e)) & 0xfu);
                             else c = (e == 0) ? __uint_as_float(word << 16) : __uint_as_float(word & 0xffff0000u);
                             dot = fmaf(c, xv[j][i * EPD + e], dot);
                         }
@@ -548,7 +573,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
                         acc = fmaf(sc, dot - xoff[j], acc);
                         acc2 = fmaf(bi, xs[j], acc2);
                     } else {
-                        acc += fmaf(sc, dot, bi * xs[j]);
+                        acc += fmaf(CB == 4 ? sc * 16777216.f : sc, dot, bi * xs[j]);
                     }
                 } else {
                     acc += dot;
