@@ -24,12 +24,12 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
     return static_cast<float>(h);
 }
 
-// Nearest-even fp32 -> bf16 (a NaN stays a quiet NaN).
+// Nearest-even fp32 -> bf16: gfx950's v_cvt_pk_bf16_f32 under the default
+// round mode (a NaN stays a NaN).  One instruction; the integer form (add
+// 0x7fff plus the kept lsb, with a NaN test) compiled to a dozen scalar and
+// vector instructions with exec-mask branching per element.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Nearest-even fp32 -> f16 (the hardware conversion rounds to nearest-even).
