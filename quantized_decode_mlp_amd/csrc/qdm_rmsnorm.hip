@@ -93,12 +93,16 @@ add_rmsnorm_kernel(const void* a, const void* b, const void* __restrict__ w,
     const int64_t base = static_cast<int64_t>(blockIdx.x) * n;
     const int t = static_cast<int>(threadIdx.x);
     const int nch = (n + CE - 1) / CE;
-    // s of chunk c, rounded once, squares accumulated in element order
-    auto sum_chunk = [&](const float (&av)[CE], const float (&bv)[CE], float (&sv)[CE], int c, float& ss) {
+    // s of chunk c, rounded once, squares accumulated in element order; a chunk
+    // that is not live (past the row, loaded at a clamped index) adds nothing.
+    // Selects, not branches: a branch around the use lets the compiler sink
+    // the chunk's loads into it and wait for each on its own.
+    auto sum_chunk = [&](const float (&av)[CE], const float (&bv)[CE], float (&sv)[CE], int c, bool live, float& ss) {
 #pragma unroll
         for (int e = 0; e < CE; ++e) {
             sv[e] = round_trip<DT>(av[e] + bv[e]);
-            if (c * CE + e < n) ss = fmaf(sv[e], sv[e], ss);
+            const float sq = fmaf(sv[e], sv[e], ss);
+            ss = live && c * CE + e < n ? sq : ss;
         }
     };
     float ss = 0.f;
@@ -114,8 +118,7 @@ add_rmsnorm_kernel(const void* a, const void* b, const void* __restrict__ w,
                 load_chunk<DT, VEC>(w, 0, c, n, wv[j]);
             }
 #pragma unroll
-            for (int j = 0; j < H; ++j)
-                if (t + j * kThreads < nch) sum_chunk(av[j], bv[j], sv[j], t + j * kThreads, ss);
+            for (int j = 0; j < H; ++j) sum_chunk(av[j], bv[j], sv[j], t + j * kThreads, t + j * kThreads < nch, ss);
         }
         const float inv = 1.0f / sqrtf(block_sum(ss) / static_cast<float>(n) + eps);
 #pragma unroll
@@ -134,7 +137,7 @@ add_rmsnorm_kernel(const void* a, const void* b, const void* __restrict__ w,
             float av[CE], bv[CE], sv[CE];
             load_chunk<DT, VEC>(a, base, c, n, av);
             load_chunk<DT, VEC>(b, base, c, n, bv);
-            sum_chunk(av, bv, sv, c, ss);
+            sum_chunk(av, bv, sv, c, true, ss);
         }
         const float inv = 1.0f / sqrtf(block_sum(ss) / static_cast<float>(n) + eps);
         for (int c = t; c < nch; c += kThreads) {
@@ -143,7 +146,7 @@ add_rmsnorm_kernel(const void* a, const void* b, const void* __restrict__ w,
             load_chunk<DT, VEC>(b, base, c, n, bv);
             load_chunk<DT, VEC>(w, 0, c, n, wv);
             float dummy = 0.f;
-            sum_chunk(av, bv, sv, c, dummy);
+            sum_chunk(av, bv, sv, c, true, dummy);
 #pragma unroll
             for (int e = 0; e < CE; ++e) nv[e] = sv[e] * inv * wv[e];
             store_chunk<DT, VEC>(s_out, base, c, n, sv);
