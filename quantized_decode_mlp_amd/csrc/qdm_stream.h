@@ -159,11 +159,13 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
     u32x4* xl = reinterpret_cast<u32x4*>(xlds);
     u32x4 xt[XU], bt, wt;
     if constexpr (NORM) {
-        if (tid < nunits) {
-            xt[0] = xg[tid];
-            bt = static_cast<const u32x4*>(ch.b)[tid];
-            wt = static_cast<const u32x4*>(ch.w)[tid];
-        }
+        // unconditional at a clamped index, with unconditional uses below: a
+        // load under a branch, or one whose only use is, ends up waited for
+        // together with the first round's weights
+        const int idx = min(tid, nunits - 1);
+        xt[0] = xg[idx];
+        bt = static_cast<const u32x4*>(ch.b)[idx];
+        wt = static_cast<const u32x4*>(ch.w)[idx];
     } else {
 #pragma unroll
         for (int u = 0; u < XU; ++u) {
@@ -230,8 +232,10 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
         for (int idx = tid + XU * NT; idx < nunits; idx += NT) xl[idx] = xg[idx];
     }
 
-    // the first round goes in flight before the activations are set up
-    if (g0 < n_grp) issue(wbuf, pbuf, g0);
+    // the first round goes in flight before the activations are set up (the
+    // chained form issues it on every path, rows clamped, so that the waits
+    // of its prologue count exactly)
+    if (NORM || g0 < n_grp) issue(wbuf, pbuf, g0);
 
     if constexpr (NORM) {
         // The decode chain's RMSNorm, recomputed by every block from a, b and w
@@ -251,7 +255,7 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
             }
             xl[idx] = sv;
         };
-        if (tid < nunits) add_piece(tid, xt[0], bt);
+        add_piece(min(tid, nunits - 1), xt[0], bt);   // threads past the row rewrite the last piece, same bytes
         for (int idx = tid + NT; idx < nunits; idx += NT) add_piece(idx, xg[idx], bg[idx]);
         __syncthreads();
         if (tid < kNormThreads) {
@@ -259,12 +263,12 @@ qgemv_stream_kernel(const uint8_t* __restrict__ q, const float* __restrict__ sb,
             constexpr int CE = norm_chunk<XDT>();
             float ss = 0.f;
             for (int c = tid; c * CE < k; c += kNormThreads) {
+                float v[CE];   // one 16-byte LDS read per chunk, squares in element order
+                load_vec<XDT, CE>(xlds, static_cast<int64_t>(c) * CE, v);
 #pragma unroll
                 for (int e = 0; e < CE; ++e) {
-                    if (c * CE + e < k) {
-                        const float sv = load_elem<XDT>(xlds, c * CE + e);
-                        ss = fmaf(sv, sv, ss);
-                    }
+                    const float sq = fmaf(v[e], v[e], ss);
+                    ss = c * CE + e < k ? sq : ss;
                 }
             }
             ss = wave_total(ss);
